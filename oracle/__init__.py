@@ -1,0 +1,224 @@
+"""CPU oracle for MXFP4 attention with UOS and PNQ -- TEST INFRASTRUCTURE.
+
+This package wraps ``mxoracle.c``, a plain and slow C implementation of
+what the MXAttention path computes (MXAttention: Data-Free Optimal Scaling
+and Pre-Normalization Quantization for MXFP4 Attention, abstract).  Only the
+test suite, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import it.  It shares no code with the HIP library and never
+imports it; the HIP library never calls it.
+
+All arrays cross the boundary as numpy arrays: bf16 tensors as ``uint16``
+bit patterns, codes and scales as ``uint8``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+MODE_OCP = 0
+MODE_UOS = 1
+MODE_NONE = 2  # identity quantizer, pins only
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mxoracle.c")
+_LIB = os.path.join(_HERE, "libmxoracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (strict IEEE: no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c99", "-D_GNU_SOURCE", "-fopenmp", "-ffp-contract=off",
+               "-Wall", "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build(force=True)
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    i64 = ctypes.c_int64
+    i32 = ctypes.c_int
+    lib.orc_bf16_to_double.argtypes = [ctypes.c_uint16]
+    lib.orc_bf16_to_double.restype = ctypes.c_double
+    lib.orc_double_to_bf16.argtypes = [ctypes.c_double]
+    lib.orc_double_to_bf16.restype = ctypes.c_uint16
+    lib.orc_double_to_bf16_array.argtypes = [P, i64, P]
+    lib.orc_double_to_bf16_array.restype = None
+    lib.orc_e2m1_encode.argtypes = [ctypes.c_double]
+    lib.orc_e2m1_encode.restype = i32
+    lib.orc_e2m1_value.argtypes = [i32, i32]
+    lib.orc_e2m1_value.restype = ctypes.c_double
+    lib.orc_block_exponent.argtypes = [ctypes.c_double, i32]
+    lib.orc_block_exponent.restype = i32
+    lib.orc_e2m1_encode_array.argtypes = [P, i64, P]
+    lib.orc_e2m1_encode_array.restype = None
+    lib.orc_block_exponent_array.argtypes = [P, i64, i32, P]
+    lib.orc_block_exponent_array.restype = None
+    lib.orc_quantize_bf16.argtypes = [P, i64, i64, i64, i32, i32, P, P]
+    lib.orc_quantize_bf16.restype = i32
+    lib.orc_quantize_f64.argtypes = [P, i64, i32, P, P]
+    lib.orc_quantize_f64.restype = i32
+    lib.orc_dequantize.argtypes = [P, P, i64, i64, P]
+    lib.orc_dequantize.restype = None
+    lib.orc_block_sse.argtypes = [P, i64, i32]
+    lib.orc_block_sse.restype = ctypes.c_double
+    lib.orc_block_sse_batch.argtypes = [P, i64, i64, i32, i32, P]
+    lib.orc_block_sse_batch.restype = None
+    lib.orc_attn_rows.argtypes = [P, P, P, i64, i64, i64, i32, i32, i64, ctypes.c_double,
+                                  P, i64, P, P, P, P]
+    lib.orc_attn_rows.restype = i32
+    lib.orc_dump.argtypes = [ctypes.c_char_p, P, P, i64, i64, i64, i32, i32]
+    lib.orc_dump.restype = i32
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray | None):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    b = _c(bits, np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16(x) -> np.ndarray:
+    """Round fp64 values to bf16 bit patterns, round-to-nearest-even."""
+    x = _c(x, np.float64)
+    out = np.empty(x.shape, np.uint16)
+    _load().orc_double_to_bf16_array(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def e2m1_encode(y: float) -> int:
+    return int(_load().orc_e2m1_encode(float(y)))
+
+
+def e2m1_value(code: int, e: int) -> float:
+    return float(_load().orc_e2m1_value(int(code), int(e)))
+
+
+def block_exponent(amax: float, mode: int) -> int:
+    return int(_load().orc_block_exponent(float(amax), int(mode)))
+
+
+def e2m1_encode_array(y) -> np.ndarray:
+    y = _c(y, np.float64).reshape(-1)
+    out = np.empty(y.size, np.uint8)
+    _load().orc_e2m1_encode_array(_ptr(y), y.size, _ptr(out))
+    return out
+
+
+def block_exponent_array(amax, mode: int) -> np.ndarray:
+    a = _c(amax, np.float64).reshape(-1)
+    out = np.empty(a.size, np.int32)
+    _load().orc_block_exponent_array(_ptr(a), a.size, int(mode), _ptr(out))
+    return out
+
+
+def n_blocks(L: int) -> int:
+    return (L + 31) // 32
+
+
+def quantize_bf16(x_bits, batch: int, rows: int, cols: int, axis: int, mode: int):
+    """Canonical MXFP4 quantization of a bf16 tensor [batch][rows][cols].
+
+    Returns (codes, scales) as flat uint8 arrays in the canonical layout:
+    axis 1 -> codes [batch][rows][nb*16], axis 0 -> codes [batch][cols][nb*16].
+    """
+    x = _c(x_bits, np.uint16).reshape(-1)
+    assert x.size == batch * rows * cols
+    nvec, L = (rows, cols) if axis == 1 else (cols, rows)
+    nb = n_blocks(L)
+    codes = np.zeros(batch * nvec * nb * 16, np.uint8)
+    scales = np.zeros(batch * nvec * nb, np.uint8)
+    rc = _load().orc_quantize_bf16(_ptr(x), batch, rows, cols, axis, mode, _ptr(codes), _ptr(scales))
+    if rc != 0:
+        raise ValueError("oracle quantize rejected its arguments")
+    return codes, scales
+
+
+def quantize_f64(x, mode: int):
+    x = _c(x, np.float64).reshape(-1)
+    nb = n_blocks(x.size)
+    codes = np.zeros(nb * 16, np.uint8)
+    scales = np.zeros(nb, np.uint8)
+    rc = _load().orc_quantize_f64(_ptr(x), x.size, mode, _ptr(codes), _ptr(scales))
+    if rc != 0:
+        raise ValueError("oracle quantize rejected its arguments")
+    return codes, scales
+
+
+def dequantize(codes, scales, nvec: int, L: int) -> np.ndarray:
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint8)
+    assert codes.size == nvec * n_blocks(L) * 16 and scales.size == nvec * n_blocks(L)
+    out = np.empty(nvec * L, np.float64)
+    _load().orc_dequantize(_ptr(codes), _ptr(scales), nvec, L, _ptr(out))
+    return out.reshape(nvec, L)
+
+
+def block_sse(x, e: int) -> float:
+    x = _c(x, np.float64).reshape(-1)
+    return float(_load().orc_block_sse(_ptr(x), x.size, int(e)))
+
+
+def block_sse_batch(blocks, e0: int, ne: int) -> np.ndarray:
+    """blocks: [nblk, n] fp64 -> sse [nblk, ne] at exponents e0..e0+ne-1."""
+    blocks = _c(blocks, np.float64)
+    nblk, n = blocks.shape
+    sse = np.empty((nblk, ne), np.float64)
+    _load().orc_block_sse_batch(_ptr(blocks), nblk, n, int(e0), int(ne), _ptr(sse))
+    return sse
+
+
+def attn_rows(q, k, v, BH: int, N: int, d: int, mode: int, pnq: bool, Bc: int,
+              softmax_scale: float, rows, want_weights: bool = False):
+    """Oracle attention for the query rows ``rows`` (flat indices into [BH*N]).
+
+    q, k, v: bf16 bit patterns, [BH][N][d].  Returns a dict with
+    ``out`` [nrows, d] fp64, ``out_bf16`` [nrows, d] uint16, ``l`` [nrows],
+    ``near_tie`` [nrows] bool and, if asked, ``weights`` [nrows, N].
+    """
+    q = _c(q, np.uint16).reshape(-1)
+    k = _c(k, np.uint16).reshape(-1)
+    v = _c(v, np.uint16).reshape(-1)
+    assert q.size == BH * N * d and k.size == q.size and v.size == q.size
+    rows = _c(rows, np.int64).reshape(-1)
+    nr = rows.size
+    out = np.empty((nr, d), np.float64)
+    lsum = np.empty(nr, np.float64)
+    flags = np.zeros(nr, np.int32)
+    weights = np.empty((nr, N), np.float64) if want_weights else None
+    rc = _load().orc_attn_rows(_ptr(q), _ptr(k), _ptr(v), BH, N, d, int(mode), int(bool(pnq)),
+                               int(Bc), float(softmax_scale), _ptr(rows), nr, _ptr(out),
+                               _ptr(lsum), _ptr(flags), _ptr(weights))
+    if rc != 0:
+        raise ValueError("oracle attention rejected its arguments")
+    res = {"out": out, "out_bf16": f64_to_bf16(out), "l": lsum, "near_tie": flags != 0}
+    if want_weights:
+        res["weights"] = weights
+    return res
+
+
+def dump(path: str, codes, scales, batch: int, nvec: int, L: int, axis: int, mode: int) -> None:
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint8)
+    rc = _load().orc_dump(path.encode(), _ptr(codes), _ptr(scales), batch, nvec, L, axis, mode)
+    if rc != 0:
+        raise OSError("oracle dump failed: %s" % path)

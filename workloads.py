@@ -1,0 +1,142 @@
+"""Seeded synthetic inputs for the MXFP4 attention path.
+
+This module holds no arithmetic of the method: only seeded random draws and
+the rounding of the drawn fp32 values to bf16 (the input format).  Both the
+GPU tests/benchmark and the CPU oracle take their inputs from here.
+
+Workloads (shapes and value structure stand in for the video diffusion
+models the MXAttention abstract evaluates on, Wan2.2 and HunyuanVideo; no
+weights, prompts or videos from those models are used or needed):
+
+  tiny     B=1, H=1,  N=256,   d=64   Q, K, V ~ N(0, 1)
+  small    B=1, H=8,  N=4096,  d=128  Q, K ~ N(0, 1) with 4 outlier channels per
+                                      head (the same 4 for Q and K) scaled x20;
+                                      V ~ N(0, 1)
+  wan      B=1, H=40, N=32760, d=128  Student-t(4) per element times a
+                                      LogNormal(0, 1) scale drawn per
+                                      (tensor, head, channel); N = 21 x 1560
+  hunyuan  B=1, H=24, N=65536, d=128  N(0, 1) with one set of floor(0.01 N)
+                                      token indices, shared by Q, K, V and all
+                                      heads, scaled x10
+  sweep    2^p elements, x = s * 2^U, U ~ Uniform(-20, 10), s = +-1
+
+Every head of every tensor has its own seed stream, so a single head can be
+regenerated without drawing the rest (the oracle checks sampled rows of the
+large workloads head by head).
+"""
+from __future__ import annotations
+
+from concurrent.futures import ThreadPoolExecutor
+import os
+
+import numpy as np
+
+CONFIGS = {
+    "tiny": dict(B=1, H=1, N=256, d=64, seed=0),
+    "small": dict(B=1, H=8, N=4096, d=128, seed=1),
+    "wan": dict(B=1, H=40, N=32760, d=128, seed=2),
+    "hunyuan": dict(B=1, H=24, N=65536, d=128, seed=3),
+}
+_CFG_ID = {"tiny": 0, "small": 1, "wan": 2, "hunyuan": 3, "custom": 4}
+_TENSOR_ID = {"q": 0, "k": 1, "v": 2}
+
+
+def f32_to_bf16(x) -> np.ndarray:
+    """Round fp32 values to bf16 bit patterns (round-to-nearest-even)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def bf16_to_f32(bits) -> np.ndarray:
+    return (np.ascontiguousarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _rng(*key) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence([int(x) for x in key]))
+
+
+def outlier_channels(name: str, seed: int, b: int, h: int, d: int) -> np.ndarray:
+    """The 4 outlier channels of head (b, h) for the 'small' workload."""
+    return _rng(seed, _CFG_ID[name], 10, b, h).choice(d, size=4, replace=False)
+
+
+def heavy_tokens(name: str, seed: int, N: int) -> np.ndarray:
+    """The shared heavy-token indices of the 'hunyuan' workload."""
+    return np.sort(_rng(seed, _CFG_ID[name], 11).choice(N, size=(N // 100), replace=False))
+
+
+def head(name: str, tensor: str, b: int, h: int, seed: int | None = None, N: int | None = None,
+         d: int | None = None) -> np.ndarray:
+    """One head of Q, K or V as bf16 bit patterns, shape [N, d]."""
+    cfg = CONFIGS.get(name, {})
+    seed = cfg["seed"] if seed is None else seed
+    N = cfg["N"] if N is None else N
+    d = cfg["d"] if d is None else d
+    dist = name if name in CONFIGS else "tiny"
+    g = _rng(seed, _CFG_ID.get(name, 4), _TENSOR_ID[tensor], b, h, N, d)
+    if dist in ("tiny",):
+        x = g.standard_normal((N, d), dtype=np.float32)
+    elif dist == "small":
+        x = g.standard_normal((N, d), dtype=np.float32)
+        if tensor in ("q", "k"):
+            x[:, outlier_channels(name, seed, b, h, d)] *= 20.0
+    elif dist == "wan":
+        chan = np.exp(g.standard_normal(d)).astype(np.float32)
+        x = g.standard_t(4.0, size=(N, d)).astype(np.float32) * chan[None, :]
+    elif dist == "hunyuan":
+        x = g.standard_normal((N, d), dtype=np.float32)
+        x[heavy_tokens(name, seed, N), :] *= 10.0
+    else:
+        raise ValueError(name)
+    return f32_to_bf16(x)
+
+
+def qkv(name: str, seed: int | None = None, B: int | None = None, H: int | None = None,
+        N: int | None = None, d: int | None = None, threads: int | None = None):
+    """Q, K, V as bf16 bit patterns, each [B, H, N, d] (uint16)."""
+    cfg = CONFIGS.get(name, {})
+    B = cfg["B"] if B is None else B
+    H = cfg["H"] if H is None else H
+    N = cfg["N"] if N is None else N
+    d = cfg["d"] if d is None else d
+    out = {t: np.empty((B, H, N, d), np.uint16) for t in ("q", "k", "v")}
+    jobs = [(t, b, h) for t in ("q", "k", "v") for b in range(B) for h in range(H)]
+
+    def fill(job):
+        t, b, h = job
+        out[t][b, h] = head(name, t, b, h, seed=seed, N=N, d=d)
+
+    nt = threads or min(16, os.cpu_count() or 1)
+    with ThreadPoolExecutor(max_workers=nt) as ex:
+        list(ex.map(fill, jobs))
+    return out["q"], out["k"], out["v"]
+
+
+def sweep(p: int, seed: int = 4, chunk_log2: int = 24) -> np.ndarray:
+    """2^p bf16 values, log-uniform magnitudes over 2^-20..2^10, random sign."""
+    n = 1 << p
+    out = np.empty(n, np.uint16)
+    csz = min(n, 1 << chunk_log2)
+
+    def fill(ci):
+        g = _rng(seed, 5, p, ci)
+        u = g.random(csz, dtype=np.float32) * 30.0 - 20.0
+        s = np.where(g.random(csz, dtype=np.float32) < 0.5, -1.0, 1.0).astype(np.float32)
+        out[ci * csz:(ci + 1) * csz] = f32_to_bf16(s * np.exp2(u))
+
+    with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(fill, range(n // csz)))
+    return out
+
+
+def sample_rows(BH: int, N: int, count: int = 512, seed: int = 7) -> np.ndarray:
+    """Seeded flat query-row indices in [0, BH*N), sorted, without repeats.
+
+    Always includes the first and last query row so the ragged query tail is
+    covered."""
+    g = _rng(seed, 6, BH, N)
+    count = min(count, BH * N)
+    rows = set(g.choice(BH * N, size=count, replace=False).tolist())
+    rows |= {0, BH * N - 1}
+    return np.array(sorted(rows), dtype=np.int64)
