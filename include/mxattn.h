@@ -1,0 +1,159 @@
+/*
+ * mxattn.h -- C ABI of the MXFP4 attention library (libmxattn.so) for AMD
+ * MI355X (gfx950).
+ *
+ * Method: "MXAttention: Data-Free Optimal Scaling and Pre-Normalization
+ * Quantization for MXFP4 Attention" (arXiv 2607.24377), abstract.  The
+ * abstract defines the pieces this library computes:
+ *   - MXFP4 quantization with power-of-two block scales, in two modes: OCP
+ *     MXFP4 (the baseline it compares against) and Universal Optimal Scaling
+ *     (UOS, the fixed data-free boundary Qmax = 7.25);
+ *   - attention whose Q.K^T and P.V products run on MXFP4 operands;
+ *   - Pre-Normalization Quantization (PNQ): the unnormalized softmax
+ *     exponentials are quantized before they are summed into the row sum, so
+ *     the row sum and P.V use the same quantized values.
+ *
+ * Number format (the abstract does not fix it; this library reads MXFP4 as
+ * OCP MX does): blocks of 32 elements, each element an E2M1 code (4 bits,
+ * bit 3 = sign, magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), each block one E8M0
+ * scale byte s meaning 2^(s-127).  Two codes per byte: element 2i of a block
+ * in bits 3:0 of byte i, element 2i+1 in bits 7:4.  Encoding rounds to the
+ * nearest magnitude, ties to the even code, saturating at 6; the sign bit of
+ * the input is kept, so a negative value that rounds to zero gives code 0x8.
+ * Block exponent e (clamped to [-127, 127], an all-zero block gives -127):
+ *   MXQ_MODE_OCP: e = floor(log2(amax)) - 2
+ *   MXQ_MODE_UOS: e = the smallest integer with amax <= 7.25 * 2^e
+ *
+ * Conventions for every call:
+ *   - Tensor pointers are DEVICE pointers (hipMalloc / torch CUDA memory) owned
+ *     by the caller, 16-byte aligned; the library never allocates or frees
+ *     device memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every call except mxq_dump only enqueues work on `stream` and returns
+ *     without waiting for it.
+ *   - Return value: MXQ_OK (0) or a negative mxq_status.  All argument checks
+ *     run on the host before anything is enqueued, so a rejected call has no
+ *     effect; a failed launch is reported as MXQ_ERR_HIP.
+ *   - Inputs must be finite bf16 values (non-finite input is a precondition
+ *     violation; the results are then unspecified).
+ *   - The library keeps no global state; calls on different streams may run
+ *     concurrently as long as they do not write the same buffers.
+ */
+#ifndef MXATTN_H
+#define MXATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MXQ_MODE_OCP = 0, MXQ_MODE_UOS = 1 } mxq_mode;
+
+typedef enum {
+    MXQ_OK = 0,
+    MXQ_ERR_INVALID_ARG = -1, /* null pointer, bad size, bad mode or axis, misaligned */
+    MXQ_ERR_UNSUPPORTED = -2, /* valid request this build does not implement (e.g. d) */
+    MXQ_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
+    MXQ_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed */
+    MXQ_ERR_IO = -5           /* mxq_dump could not write its file */
+} mxq_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *mxq_status_string(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int mxattn_version(void);
+
+/*
+ * mxq_quantize -- MXFP4 quantization of a bf16 tensor (MXAttention abstract:
+ * OCP MXFP4 baseline and UOS).
+ *
+ * x_bf16: bf16 values viewed as [batch][rows][cols], contiguous.
+ * axis:   1 -> blocks of 32 run along cols (the contiguous axis);
+ *         0 -> blocks of 32 run along rows (one column at a time).
+ * Output (canonical, block-axis-major), nb = number of 32-blocks per vector:
+ *   axis 1: codes [batch][rows][nb*16] bytes, scales [batch][rows][nb], nb = ceil(cols/32)
+ *   axis 0: codes [batch][cols][nb*16] bytes, scales [batch][cols][nb], nb = ceil(rows/32)
+ * A partial last block is zero-padded (padding codes are 0; the scale comes
+ * from the valid elements only).  Empty tensors (any size 0) are a no-op.
+ * Errors: MXQ_ERR_INVALID_ARG for a null pointer with a non-empty tensor,
+ * negative sizes, axis not 0/1, mode not OCP/UOS, or a pointer that is not
+ * 16-byte aligned (x and codes; scales may have any alignment).
+ */
+int mxq_quantize(const void *x_bf16, int64_t batch, int64_t rows, int64_t cols, int axis,
+                 int mode, uint8_t *codes, uint8_t *scales, void *stream);
+
+/*
+ * mxattn_kv_tile -- number of keys per key tile of the attention kernel for
+ * head dimension d (0 if d is unsupported).  The running row maximum is
+ * updated once per key tile, in ascending key order, and the quantized
+ * exponentials are formed against that running maximum; the key tile is
+ * therefore part of the definition of the result (the abstract only speaks of
+ * "the softmax loop"; this is the flash-attention reading).
+ */
+int mxattn_kv_tile(int64_t d);
+
+/* Bytes of device workspace mxattn_fwd needs for these sizes (0 on bad sizes). */
+size_t mxattn_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d);
+
+/*
+ * mxattn_fwd -- non-causal MXFP4 attention forward (MXAttention abstract:
+ * MXFP4 Q.K^T, online softmax with PNQ, MXFP4 P.V).
+ *
+ * q, k, v, o: bf16 [B][H][N][d], contiguous.  d in {64, 128}; N >= 1.
+ * mode: block-scale rule for Q, K, V and for the softmax exponentials.
+ * pnq:  1 -> the row sum adds the quantized exponentials (PNQ);
+ *       0 -> it adds the unquantized fp32 exponentials (P.V still uses the
+ *            quantized ones; this is the normalization error PNQ removes).
+ * softmax_scale: multiplies Q.K^T; <= 0 selects 1/sqrt(d).
+ * Steps on `stream`: quantize Q and K along d and V along N into the
+ * workspace (mxq_quantize layouts with batch = B*H: Q/K axis 1 with rows = N,
+ * cols = d; V axis 0 with rows = N, cols = d), then one fused kernel.  For
+ * every query row and key tile of mxattn_kv_tile(d) keys: S = Q_q K_q^T
+ * (fp32), times softmax_scale; running max m; p = exp(s - m) in fp32;
+ * p quantized in 32-key blocks aligned to the key index (scale rule = mode);
+ * l = alpha*l + sum(p_q or p); O = alpha*O + p_q V_q; finally O/l rounded to
+ * bf16 (round to nearest even).
+ * workspace: device memory of at least mxattn_workspace_bytes(B, H, N, d).
+ * Errors: MXQ_ERR_INVALID_ARG (null or misaligned pointer, B/H < 1, N < 1,
+ * bad mode or pnq), MXQ_ERR_UNSUPPORTED (d not 64/128, or B*H*N*d too large),
+ * MXQ_ERR_WORKSPACE, MXQ_ERR_HIP.
+ */
+int mxattn_fwd(const void *q, const void *k, const void *v, int64_t B, int64_t H, int64_t N,
+               int64_t d, int mode, int pnq, float softmax_scale, void *o, void *workspace,
+               size_t workspace_bytes, void *stream);
+
+/*
+ * mxattn_fwd_quantized -- the fused kernel alone, on operands already in the
+ * canonical layouts of mxq_quantize (batch = B*H):
+ *   qc, kc: [B*H][N][d/2], qs, ks: [B*H][N][d/32]   (axis 1, rows = N, cols = d)
+ *   vc: [B*H][d][ceil(N/32)*16], vs: [B*H][d][ceil(N/32)]   (axis 0)
+ * mode is the scale rule used for the softmax exponentials.  Other arguments
+ * and errors as mxattn_fwd (no workspace).
+ */
+int mxattn_fwd_quantized(const uint8_t *qc, const uint8_t *qs, const uint8_t *kc, const uint8_t *ks,
+                         const uint8_t *vc, const uint8_t *vs, int64_t B, int64_t H, int64_t N,
+                         int64_t d, int mode, int pnq, float softmax_scale, void *o, void *stream);
+
+/*
+ * mxq_dump -- write quantized data in the reference format "MXQ1": a 256-byte
+ * header of ASCII JSON padded with spaces and ending in '\n'
+ *   {"magic":"MXQ1","version":1,"mode":"ocp"|"uos","axis":A,"batch":B,
+ *    "nvec":V,"L":L,"block":32,"elem":"e2m1","scale":"e8m0","nibble":"lo-first"}
+ * followed by batch*nvec*ceil(L/32)*16 code bytes and batch*nvec*ceil(L/32)
+ * scale bytes in the canonical layout (nvec = vectors per batch entry, L =
+ * their length: rows/cols for axis 1, cols/rows for axis 0).
+ * codes/scales may be device pointers (copied on `stream`, which is then
+ * synchronized) or host pointers (read directly).  Synchronous.
+ * Errors: MXQ_ERR_INVALID_ARG, MXQ_ERR_HIP (copy failed), MXQ_ERR_IO.
+ */
+int mxq_dump(const char *path, const uint8_t *codes, const uint8_t *scales, int64_t batch,
+             int64_t nvec, int64_t L, int axis, int mode, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXATTN_H */

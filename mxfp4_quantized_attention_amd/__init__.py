@@ -1,0 +1,169 @@
+"""MXFP4 attention with UOS and PNQ on AMD MI355X (gfx950).
+
+Thin Python binding of ``libmxattn.so`` (C ABI in ``include/mxattn.h``):
+argument marshalling only.  Every step of the computation runs in the HIP
+kernels of that library; PyTorch is used only to allocate device memory and
+to name the current stream.  If the library has not been built, importing the
+binding works but every call raises.
+
+Method: "MXAttention: Data-Free Optimal Scaling and Pre-Normalization
+Quantization for MXFP4 Attention" (arXiv 2607.24377), abstract.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+MODE_OCP = 0
+MODE_UOS = 1
+_MODES = {"ocp": MODE_OCP, "uos": MODE_UOS, MODE_OCP: MODE_OCP, MODE_UOS: MODE_UOS}
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxattn.so")
+_lib = None
+
+
+class MXAttnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what} failed: {status_string(status)} ({status})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m mxfp4_quantized_attention_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+    L.mxq_status_string.argtypes = [i32]
+    L.mxq_status_string.restype = ctypes.c_char_p
+    L.mxattn_version.argtypes = []
+    L.mxattn_version.restype = i32
+    L.mxq_quantize.argtypes = [P, i64, i64, i64, i32, i32, P, P, P]
+    L.mxq_quantize.restype = i32
+    L.mxattn_kv_tile.argtypes = [i64]
+    L.mxattn_kv_tile.restype = i32
+    L.mxattn_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    L.mxattn_workspace_bytes.restype = ctypes.c_size_t
+    L.mxattn_fwd.argtypes = [P, P, P, i64, i64, i64, i64, i32, i32, f32, P, P, ctypes.c_size_t, P]
+    L.mxattn_fwd.restype = i32
+    L.mxattn_fwd_quantized.argtypes = [P, P, P, P, P, P, i64, i64, i64, i64, i32, i32, f32, P, P]
+    L.mxattn_fwd_quantized.restype = i32
+    L.mxq_dump.argtypes = [ctypes.c_char_p, P, P, i64, i64, i64, i32, i32, P]
+    L.mxq_dump.restype = i32
+    _lib = L
+    return L
+
+
+EXPORTS = ("mxq_status_string", "mxattn_version", "mxq_quantize", "mxattn_kv_tile",
+           "mxattn_workspace_bytes", "mxattn_fwd", "mxattn_fwd_quantized", "mxq_dump")
+
+
+def status_string(status: int) -> str:
+    return lib().mxq_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return int(lib().mxattn_version())
+
+
+def kv_tile(d: int) -> int:
+    return int(lib().mxattn_kv_tile(int(d)))
+
+
+def workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    return int(lib().mxattn_workspace_bytes(B, H, N, d))
+
+
+def _mode(mode) -> int:
+    if mode not in _MODES:
+        raise ValueError(f"mode must be 'ocp' or 'uos', got {mode!r}")
+    return _MODES[mode]
+
+
+def _stream(t):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise MXAttnError(status, what)
+
+
+def _bf16_device(t, name):
+    import torch
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or not t.is_cuda:
+        raise TypeError(f"{name} must be a bfloat16 CUDA tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def n_blocks(L: int) -> int:
+    return (L + 31) // 32
+
+
+def quantize(x, mode="uos", axis: int = 1):
+    """MXFP4-quantize a bf16 tensor viewed as [batch][rows][cols].
+
+    x may have any rank >= 2: the last two dimensions are rows and cols, the
+    rest is batch.  Returns (codes, scales) as uint8 tensors in the canonical
+    layout of ``mxq_quantize`` (axis 1: [batch, rows, nb*16] / [batch, rows, nb];
+    axis 0: [batch, cols, nb*16] / [batch, cols, nb]).
+    """
+    import torch
+    x = _bf16_device(x, "x")
+    if x.dim() < 2:
+        raise ValueError("x needs at least 2 dimensions")
+    rows, cols = x.shape[-2], x.shape[-1]
+    batch = x.numel() // max(1, rows * cols) if rows * cols else math.prod(x.shape[:-2])
+    nvec, L = (rows, cols) if axis == 1 else (cols, rows)
+    nb = n_blocks(L)
+    codes = torch.empty((batch, nvec, nb * 16), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((batch, nvec, nb), dtype=torch.uint8, device=x.device)
+    _check(lib().mxq_quantize(x.data_ptr(), batch, rows, cols, int(axis), _mode(mode),
+                              codes.data_ptr(), scales.data_ptr(), _stream(x)), "mxq_quantize")
+    return codes, scales
+
+
+def fwd(q, k, v, mode="uos", pnq: bool = True, softmax_scale: float = 0.0, workspace=None, out=None):
+    """Non-causal MXFP4 attention.  q, k, v: bf16 [B, H, N, d] -> o bf16 [B, H, N, d]."""
+    import torch
+    q, k, v = (_bf16_device(t, n) for t, n in ((q, "q"), (k, "k"), (v, "v")))
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must all be [B, H, N, d]")
+    B, H, N, d = q.shape
+    need = workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q) if out is None else out
+    _check(lib().mxattn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, N, d, _mode(mode),
+                            int(bool(pnq)), float(softmax_scale), o.data_ptr(), workspace.data_ptr(),
+                            workspace.numel(), _stream(q)), "mxattn_fwd")
+    return o
+
+
+def fwd_quantized(qc, qs, kc, ks, vc, vs, B: int, H: int, N: int, d: int, mode="uos",
+                  pnq: bool = True, softmax_scale: float = 0.0, out=None):
+    """The fused kernel on operands already quantized by ``quantize`` (Q, K along
+    d with axis 1; V along N with axis 0, batch = B*H)."""
+    import torch
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=qc.device) if out is None else out
+    _check(lib().mxattn_fwd_quantized(qc.data_ptr(), qs.data_ptr(), kc.data_ptr(), ks.data_ptr(),
+                                      vc.data_ptr(), vs.data_ptr(), B, H, N, d, _mode(mode),
+                                      int(bool(pnq)), float(softmax_scale), o.data_ptr(), _stream(qc)),
+           "mxattn_fwd_quantized")
+    return o
+
+
+def dump(path: str, codes, scales, batch: int, nvec: int, L: int, axis: int, mode="uos") -> None:
+    """Write (codes, scales) in the "MXQ1" reference format (synchronous)."""
+    import torch
+    stream = _stream(codes) if isinstance(codes, torch.Tensor) and codes.is_cuda else None
+    _check(lib().mxq_dump(path.encode(), codes.data_ptr(), scales.data_ptr(), batch, nvec, L,
+                          int(axis), _mode(mode), stream), "mxq_dump")

@@ -1,0 +1,203 @@
+// abi.hip -- the C ABI of libmxattn.so (declared in include/mxattn.h).
+//
+// Every entry point validates its arguments on the host before touching the
+// HIP runtime, so a rejected call enqueues nothing and needs no GPU.  Work is
+// enqueued on the caller's stream; the library allocates no device memory.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "mxattn.h"
+
+namespace mxattn {
+hipError_t launch_quantize(const void* x, int64_t batch, int64_t rows, int64_t cols, int axis,
+                           int mode, uint8_t* codes, uint8_t* scales, hipStream_t stream);
+hipError_t launch_attention(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
+                            const uint8_t* vc, const uint8_t* vs, int BH, int N, int d, int mode,
+                            bool pnq, float softmax_scale, uint16_t* o, hipStream_t stream);
+}  // namespace mxattn
+
+namespace {
+
+constexpr int64_t kMaxElems = int64_t(1) << 40;  // per quantize call
+constexpr int64_t kMaxAttnElems = int64_t(1) << 34;  // B*H*N*d per attention call
+constexpr int kKvTile = 128;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool valid_mode(int mode) { return mode == MXQ_MODE_OCP || mode == MXQ_MODE_UOS; }
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct WsLayout {
+  size_t qc, qs, kc, ks, vc, vs, total;
+};
+
+// Workspace regions (each 256-byte aligned): Q codes/scales, K codes/scales
+// (axis 1, rows = N, cols = d) and V codes/scales (axis 0).
+WsLayout ws_layout(int64_t BH, int64_t N, int64_t d) {
+  WsLayout w;
+  const size_t qcb = size_t(BH * N * d / 2), qsb = size_t(BH * N * (d / 32));
+  const int64_t nbn = (N + 31) / 32;
+  const size_t vcb = size_t(BH * d * nbn * 16), vsb = size_t(BH * d * nbn);
+  size_t off = 0;
+  w.qc = off; off = round256(off + qcb);
+  w.qs = off; off = round256(off + qsb);
+  w.kc = off; off = round256(off + qcb);
+  w.ks = off; off = round256(off + qsb);
+  w.vc = off; off = round256(off + vcb);
+  w.vs = off; off = round256(off + vsb);
+  w.total = off;
+  return w;
+}
+
+int check_attn_sizes(int64_t B, int64_t H, int64_t N, int64_t d) {
+  if (B < 1 || H < 1 || N < 1) return MXQ_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return MXQ_ERR_UNSUPPORTED;
+  if (B > (int64_t(1) << 20) || H > (int64_t(1) << 20) || N > (int64_t(1) << 26)) return MXQ_ERR_UNSUPPORTED;
+  const int64_t BH = B * H;
+  if (BH > (int64_t(1) << 24) || BH * N * d > kMaxAttnElems) return MXQ_ERR_UNSUPPORTED;
+  // the workgroup count (BH * ceil(N / 256), rounded to 8) must fit an int
+  if (BH * ((N + 255) / 256) + 8 > (int64_t(1) << 31) - 1) return MXQ_ERR_UNSUPPORTED;
+  return MXQ_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MXQ_OK : MXQ_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* mxq_status_string(int status) {
+  switch (status) {
+    case MXQ_OK: return "MXQ_OK";
+    case MXQ_ERR_INVALID_ARG: return "MXQ_ERR_INVALID_ARG";
+    case MXQ_ERR_UNSUPPORTED: return "MXQ_ERR_UNSUPPORTED";
+    case MXQ_ERR_WORKSPACE: return "MXQ_ERR_WORKSPACE";
+    case MXQ_ERR_HIP: return "MXQ_ERR_HIP";
+    case MXQ_ERR_IO: return "MXQ_ERR_IO";
+    default: return "MXQ_ERR_UNKNOWN";
+  }
+}
+
+int mxattn_version(void) { return 100; }
+
+int mxq_quantize(const void* x_bf16, int64_t batch, int64_t rows, int64_t cols, int axis, int mode,
+                 uint8_t* codes, uint8_t* scales, void* stream) {
+  if (batch < 0 || rows < 0 || cols < 0 || (axis != 0 && axis != 1) || !valid_mode(mode))
+    return MXQ_ERR_INVALID_ARG;
+  if (batch == 0 || rows == 0 || cols == 0) return MXQ_OK;
+  if (!x_bf16 || !codes || !scales) return MXQ_ERR_INVALID_ARG;
+  if (!aligned16(x_bf16) || !aligned16(codes)) return MXQ_ERR_INVALID_ARG;
+  if (rows > kMaxElems || cols > kMaxElems || batch > kMaxElems || rows * cols > kMaxElems ||
+      batch * rows * cols > kMaxElems)
+    return MXQ_ERR_UNSUPPORTED;
+  if (axis == 0 && batch > 65535) return MXQ_ERR_UNSUPPORTED;
+  if (axis == 0 && ((rows + 255) / 256) * ((cols + 63) / 64) > 0x7FFFFFFF) return MXQ_ERR_UNSUPPORTED;
+  if (axis == 1 && (cols & 31) != 0 && (batch * rows * ((cols + 31) / 32) + 255) / 256 > 0x7FFFFFFF)
+    return MXQ_ERR_UNSUPPORTED;
+  return hip_status(mxattn::launch_quantize(x_bf16, batch, rows, cols, axis, mode, codes, scales,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int mxattn_kv_tile(int64_t d) { return (d == 64 || d == 128) ? kKvTile : 0; }
+
+size_t mxattn_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
+  if (check_attn_sizes(B, H, N, d) != MXQ_OK) return 0;
+  return ws_layout(B * H, N, d).total;
+}
+
+int mxattn_fwd_quantized(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
+                         const uint8_t* vc, const uint8_t* vs, int64_t B, int64_t H, int64_t N,
+                         int64_t d, int mode, int pnq, float softmax_scale, void* o, void* stream) {
+  int st = check_attn_sizes(B, H, N, d);
+  if (st != MXQ_OK) return st;
+  if (!valid_mode(mode) || (pnq != 0 && pnq != 1) || !std::isfinite(softmax_scale)) return MXQ_ERR_INVALID_ARG;
+  if (!qc || !qs || !kc || !ks || !vc || !vs || !o) return MXQ_ERR_INVALID_ARG;
+  if (!aligned16(qc) || !aligned16(kc) || !aligned16(vc) || !aligned16(o)) return MXQ_ERR_INVALID_ARG;
+  const float scale = softmax_scale > 0.f ? softmax_scale : float(1.0 / std::sqrt(double(d)));
+  return hip_status(mxattn::launch_attention(qc, qs, kc, ks, vc, vs, int(B * H), int(N), int(d), mode,
+                                             pnq != 0, scale, static_cast<uint16_t*>(o),
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int mxattn_fwd(const void* q, const void* k, const void* v, int64_t B, int64_t H, int64_t N, int64_t d,
+               int mode, int pnq, float softmax_scale, void* o, void* workspace, size_t workspace_bytes,
+               void* stream) {
+  int st = check_attn_sizes(B, H, N, d);
+  if (st != MXQ_OK) return st;
+  if (!valid_mode(mode) || (pnq != 0 && pnq != 1) || !std::isfinite(softmax_scale)) return MXQ_ERR_INVALID_ARG;
+  if (!q || !k || !v || !o) return MXQ_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return MXQ_ERR_INVALID_ARG;
+  const int64_t BH = B * H;
+  const WsLayout w = ws_layout(BH, N, d);
+  if (!workspace || workspace_bytes < w.total) return MXQ_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return MXQ_ERR_INVALID_ARG;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = mxattn::launch_quantize(q, BH, N, d, 1, mode, ws + w.qc, ws + w.qs, s);
+  if (e == hipSuccess) e = mxattn::launch_quantize(k, BH, N, d, 1, mode, ws + w.kc, ws + w.ks, s);
+  if (e == hipSuccess) e = mxattn::launch_quantize(v, BH, N, d, 0, mode, ws + w.vc, ws + w.vs, s);
+  if (e != hipSuccess) return MXQ_ERR_HIP;
+  const float scale = softmax_scale > 0.f ? softmax_scale : float(1.0 / std::sqrt(double(d)));
+  return hip_status(mxattn::launch_attention(ws + w.qc, ws + w.qs, ws + w.kc, ws + w.ks, ws + w.vc, ws + w.vs,
+                                             int(BH), int(N), int(d), mode, pnq != 0, scale,
+                                             static_cast<uint16_t*>(o), s));
+}
+
+int mxq_dump(const char* path, const uint8_t* codes, const uint8_t* scales, int64_t batch, int64_t nvec,
+             int64_t L, int axis, int mode, void* stream) {
+  if (!path || batch < 0 || nvec < 0 || L < 0 || (axis != 0 && axis != 1) || !valid_mode(mode))
+    return MXQ_ERR_INVALID_ARG;
+  if (batch > kMaxElems || nvec > kMaxElems || L > kMaxElems || batch * nvec > kMaxElems ||
+      batch * nvec * ((L + 31) / 32) > kMaxElems / 16)
+    return MXQ_ERR_INVALID_ARG;
+  const int64_t nb = (L + 31) / 32;
+  const size_t ncode = size_t(batch * nvec * nb * 16), nscale = size_t(batch * nvec * nb);
+  if ((ncode > 0) && (!codes || !scales)) return MXQ_ERR_INVALID_ARG;
+  char hdr[256];
+  const int len = std::snprintf(hdr, sizeof hdr,
+                                "{\"magic\":\"MXQ1\",\"version\":1,\"mode\":\"%s\",\"axis\":%d,\"batch\":%lld,"
+                                "\"nvec\":%lld,\"L\":%lld,\"block\":32,\"elem\":\"e2m1\",\"scale\":\"e8m0\","
+                                "\"nibble\":\"lo-first\"}",
+                                mode == MXQ_MODE_OCP ? "ocp" : "uos", axis, (long long)batch,
+                                (long long)nvec, (long long)L);
+  if (len < 0 || len > 254) return MXQ_ERR_INVALID_ARG;
+  std::memset(hdr + len, ' ', size_t(255 - len));
+  hdr[255] = '\n';
+
+  // Device pointers are copied on the caller's stream; host memory (or any
+  // pointer the runtime does not know) is read directly.
+  std::vector<uint8_t> hc, hs;
+  const uint8_t* pc = codes;
+  const uint8_t* ps = scales;
+  if (ncode > 0) {
+    hipPointerAttribute_t attr;
+    bool on_device = false;
+    if (hipPointerGetAttributes(&attr, codes) == hipSuccess)
+      on_device = attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged;
+    else
+      (void)hipGetLastError();  // unknown pointer: treat as host memory
+    if (on_device) {
+      hc.resize(ncode);
+      hs.resize(nscale);
+      hipStream_t s = static_cast<hipStream_t>(stream);
+      if (hipMemcpyAsync(hc.data(), codes, ncode, hipMemcpyDeviceToHost, s) != hipSuccess ||
+          hipMemcpyAsync(hs.data(), scales, nscale, hipMemcpyDeviceToHost, s) != hipSuccess ||
+          hipStreamSynchronize(s) != hipSuccess)
+        return MXQ_ERR_HIP;
+      pc = hc.data();
+      ps = hs.data();
+    }
+  }
+  FILE* f = std::fopen(path, "wb");
+  if (!f) return MXQ_ERR_IO;
+  bool ok = std::fwrite(hdr, 1, 256, f) == 256;
+  if (ok && ncode) ok = std::fwrite(pc, 1, ncode, f) == ncode;
+  if (ok && nscale) ok = std::fwrite(ps, 1, nscale, f) == nscale;
+  ok = (std::fclose(f) == 0) && ok;
+  return ok ? MXQ_OK : MXQ_ERR_IO;
+}
+
+}  // extern "C"

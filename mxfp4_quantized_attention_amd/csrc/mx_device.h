@@ -1,0 +1,70 @@
+// mx_device.h -- gfx950 device helpers shared by the MXFP4 kernels.
+//
+// MXFP4 as read from the MXAttention abstract (arXiv 2607.24377): 32-element
+// blocks, E2M1 elements, one E8M0 power-of-two scale per block.  The block
+// exponent rules are OCP MXFP4 (e = floor(log2 amax) - 2) and UOS with the
+// boundary Qmax = 7.25 (e = smallest integer with amax <= 7.25 * 2^e).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxattn {
+
+enum : int { kModeOCP = 0, kModeUOS = 1 };
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// Block exponent from the bit pattern of a non-negative fp32 amax.
+// amax = 2^E * M, M in [1, 2): OCP e = E - 2; UOS e = E - 2 + [M > 1.8125],
+// which is the least e with amax <= 7.25 * 2^e (7.25 = 1.8125 * 4).  1.8125
+// is mantissa field 0x680000.  A zero or subnormal amax has exponent field 0
+// and lands below -127, where the clamp puts it.
+template <int MODE>
+__device__ __forceinline__ int block_exp_f32bits(uint32_t bits) {
+  int E = int((bits >> 23) & 0xFFu) - 127;
+  int e = E - 2;
+  if (MODE == kModeUOS) e += (bits & 0x7FFFFFu) > 0x680000u ? 1 : 0;
+  e = e < -127 ? -127 : e;
+  e = e > 127 ? 127 : e;
+  return e;
+}
+
+// Same rule from the bit pattern of a non-negative bf16 amax (7 mantissa bits;
+// 1.8125 is mantissa field 0x68).
+template <int MODE>
+__device__ __forceinline__ int block_exp_bf16bits(uint32_t bits) {
+  int E = int((bits >> 7) & 0xFFu) - 127;
+  int e = E - 2;
+  if (MODE == kModeUOS) e += (bits & 0x7Fu) > 0x68u ? 1 : 0;
+  e = e < -127 ? -127 : e;
+  e = e > 127 ? 127 : e;
+  return e;
+}
+
+// 2^e as an fp32 value for e in [-126, 127].
+__device__ __forceinline__ float pow2f(int e) { return __uint_as_float(uint32_t(e + 127) << 23); }
+
+// Two fp32 values -> two E2M1 codes in byte `SEL` of `old`, each value divided
+// by the power of two `scale` first.  The hardware rounds to nearest, ties to
+// the even code, saturates at 6 and keeps the sign of values that round to 0.
+template <int SEL>
+__device__ __forceinline__ uint32_t cvt_fp4x2(uint32_t old, float a, float b, float scale) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, scale, SEL);
+}
+
+// One 16x16x128 MFMA on FP4 operands with E8M0 block scales.
+// A (16 rows x 128 K): lane l holds row l%16, K = 32*(l/16) + [0, 32) as 32
+// nibbles in a[0..3] (nibble n of the 128 bits = K offset n).  B (128 K x 16
+// cols): lane l holds col l%16 with the same K slice.  C/D: lane l holds col
+// l%16, rows 4*(l/16) + [0, 4).  sa/sb: the E8M0 scale byte of the lane's
+// 32-element K slice (byte 0 of the register).
+__device__ __forceinline__ v4f mfma_fp4_16x16x128(const uint4& a, const uint4& b, v4f c,
+                                                    int sa, int sb) {
+  v8i A = {int(a.x), int(a.y), int(a.z), int(a.w), 0, 0, 0, 0};
+  v8i B = {int(b.x), int(b.y), int(b.z), int(b.w), 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, c, 4, 4, 0, sa, 0, sb);
+}
+
+}  // namespace mxattn

@@ -1,0 +1,225 @@
+// quantize.hip -- bf16 -> MXFP4 (E2M1 codes + E8M0 block scales) for gfx950.
+//
+// MXAttention (arXiv 2607.24377), abstract: MXFP4 with power-of-two block
+// scales; OCP MXFP4 is the baseline rule, UOS the fixed boundary Qmax = 7.25.
+// This pass is a streaming codec bound by HBM bandwidth: 2 bytes read and
+// 0.5 + 1/32 bytes written per element.
+//
+// Encoding: for a block with exponent e, y = x / 2^e is rounded to the nearest
+// E2M1 magnitude (ties to the even code, saturating at 6, sign kept).  The
+// division is exact; v_cvt_scalef32_pk_fp4_f32 performs it through its scale
+// operand and rounds.  For e <= -125 a subnormal input could round to a
+// non-zero code, so those (rare) blocks are first multiplied by 2^-e in fp32,
+// which makes every non-zero y normal, and converted with scale 1.
+#include "mx_device.h"
+
+namespace mxattn {
+
+namespace {
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Eight fp32 values, block exponent e -> eight codes (element 2i in nibble 2i).
+__device__ __forceinline__ uint32_t encode8(float f0, float f1, float f2, float f3, float f4,
+                                            float f5, float f6, float f7, int e) {
+  float scale;
+  if (e >= -124) {
+    scale = pow2f(e);
+  } else {
+    const float up = pow2f(-e);  // -e in [124, 127]
+    f0 *= up; f1 *= up; f2 *= up; f3 *= up; f4 *= up; f5 *= up; f6 *= up; f7 *= up;
+    scale = 1.0f;
+  }
+  uint32_t r = 0;
+  r = cvt_fp4x2<0>(r, f0, f1, scale);
+  r = cvt_fp4x2<1>(r, f2, f3, scale);
+  r = cvt_fp4x2<2>(r, f4, f5, scale);
+  r = cvt_fp4x2<3>(r, f6, f7, scale);
+  return r;
+}
+
+__device__ __forceinline__ uint32_t encode8_bf16(const uint4& v, int e) {
+  return encode8(bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y), bf16lo(v.z), bf16hi(v.z),
+                 bf16lo(v.w), bf16hi(v.w), e);
+}
+
+// Largest |x| bit pattern of the 8 bf16 values in v (non-negative floats
+// order like their bit patterns).
+__device__ __forceinline__ uint32_t absmax8_bits(const uint4& v) {
+  const uint32_t m = 0x7FFF7FFFu;
+  uint32_t a = v.x & m, b = v.y & m, c = v.z & m, d = v.w & m;
+  auto mx = [](uint32_t p, uint32_t q) {
+    uint32_t lo = max(p & 0xFFFFu, q & 0xFFFFu);
+    uint32_t hi = max(p >> 16, q >> 16);
+    return lo | (hi << 16);
+  };
+  uint32_t t = mx(mx(a, b), mx(c, d));
+  return max(t & 0xFFFFu, t >> 16);
+}
+
+}  // namespace
+
+// Flat stream of full 32-element blocks: block i = elements [32i, 32i + 32)
+// of x, codes [16i, 16i + 16), scale [i].  Four lanes share a block (16 bytes
+// of input each), so a wave reads 1 KiB and writes 256 code bytes per step,
+// both contiguous.  nq = 4 * number of blocks.
+template <int MODE, int U>
+__global__ __launch_bounds__(256) void quant_stream_kernel(const uint4* __restrict__ x,
+                                                           uint32_t* __restrict__ codes,
+                                                           uint8_t* __restrict__ scales,
+                                                           int64_t nq) {
+  const int64_t step = int64_t(gridDim.x) * 256 * U;
+  for (int64_t base = int64_t(blockIdx.x) * 256 * U + threadIdx.x; base < nq; base += step) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t idx = base + int64_t(u) * 256;
+      v[u] = idx < nq ? x[idx] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t idx = base + int64_t(u) * 256;
+      uint32_t m = absmax8_bits(v[u]);
+      // max over the 4 lanes of the quad: quad_perm [1,0,3,2] then [2,3,0,1]
+      m = max(m, uint32_t(__builtin_amdgcn_mov_dpp(int(m), 0xB1, 0xF, 0xF, true)));
+      m = max(m, uint32_t(__builtin_amdgcn_mov_dpp(int(m), 0x4E, 0xF, 0xF, true)));
+      const int e = block_exp_bf16bits<MODE>(m);
+      const uint32_t c = encode8_bf16(v[u], e);
+      if (idx < nq) {
+        codes[idx] = c;
+        if ((idx & 3) == 0) scales[idx >> 2] = uint8_t(e + 127);
+      }
+    }
+  }
+}
+
+// Blocks along the contiguous axis when cols is not a multiple of 32: one
+// thread per block, element loads with bounds checks, zero padding.
+template <int MODE>
+__global__ __launch_bounds__(256) void quant_rows_general_kernel(const uint16_t* __restrict__ x,
+                                                                 uint4* __restrict__ codes,
+                                                                 uint8_t* __restrict__ scales,
+                                                                 int64_t nvec, int64_t L, int64_t nb) {
+  const int64_t b = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (b >= nvec * nb) return;
+  const int64_t vec = b / nb, blk = b % nb;
+  const uint16_t* src = x + vec * L + blk * 32;
+  const int n = int(min(int64_t(32), L - blk * 32));
+  float f[32];
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const uint32_t h = i < n ? uint32_t(src[i]) : 0u;
+    m = max(m, h & 0x7FFFu);
+    f[i] = __uint_as_float(h << 16);
+  }
+  const int e = block_exp_bf16bits<MODE>(m);
+  uint4 c;
+  c.x = encode8(f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7], e);
+  c.y = encode8(f[8], f[9], f[10], f[11], f[12], f[13], f[14], f[15], e);
+  c.z = encode8(f[16], f[17], f[18], f[19], f[20], f[21], f[22], f[23], e);
+  c.w = encode8(f[24], f[25], f[26], f[27], f[28], f[29], f[30], f[31], e);
+  codes[b] = c;
+  scales[b] = uint8_t(e + 127);
+}
+
+// Blocks along rows (axis 0), one column at a time: a 256-row x 64-column
+// bf16 tile is staged in LDS with row-contiguous loads, then each (column,
+// 32-row block) is encoded from LDS and written to the column-major output
+// codes [batch][cols][nb*16].  Rows past the end are zero (padding).
+template <int MODE>
+__global__ __launch_bounds__(256) void quant_cols_kernel(const uint16_t* __restrict__ x,
+                                                         uint8_t* __restrict__ codes,
+                                                         uint8_t* __restrict__ scales, int64_t rows,
+                                                         int64_t cols, int64_t nb, int64_t ntc) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[256 * 64];
+  const int64_t bi = blockIdx.y;
+  const int64_t tr = blockIdx.x / ntc, tc = blockIdx.x % ntc;
+  const int64_t r0 = tr * 256, c0 = tc * 64;
+  const uint16_t* xb = x + bi * rows * cols;
+  const int tid = threadIdx.x;
+  if ((cols & 7) == 0) {
+    const int cc = (tid & 7) * 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int rr = (tid >> 3) + 32 * i;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (r0 + rr < rows && c0 + cc < cols)
+        v = *reinterpret_cast<const uint4*>(xb + (r0 + rr) * cols + c0 + cc);
+      *reinterpret_cast<uint4*>(&tile[rr * 64 + cc]) = v;
+    }
+  } else {
+    for (int i = tid; i < 256 * 64; i += 256) {
+      const int rr = i >> 6, cc = i & 63;
+      tile[i] = (r0 + rr < rows && c0 + cc < cols) ? xb[(r0 + rr) * cols + c0 + cc] : uint16_t(0);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int item = tid + 256 * k;
+    const int c = item & 63, jb = item >> 6;
+    const int64_t blk = tr * 8 + jb;
+    if (c0 + c >= cols || blk >= nb) continue;
+    float f[32];
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const uint32_t h = tile[(32 * jb + i) * 64 + c];
+      m = max(m, h & 0x7FFFu);
+      f[i] = __uint_as_float(h << 16);
+    }
+    const int e = block_exp_bf16bits<MODE>(m);
+    uint4 cw;
+    cw.x = encode8(f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7], e);
+    cw.y = encode8(f[8], f[9], f[10], f[11], f[12], f[13], f[14], f[15], e);
+    cw.z = encode8(f[16], f[17], f[18], f[19], f[20], f[21], f[22], f[23], e);
+    cw.w = encode8(f[24], f[25], f[26], f[27], f[28], f[29], f[30], f[31], e);
+    const int64_t vec = bi * cols + c0 + c;
+    *reinterpret_cast<uint4*>(codes + (vec * nb + blk) * 16) = cw;
+    scales[vec * nb + blk] = uint8_t(e + 127);
+  }
+}
+
+// Host-side launchers (stream-ordered, no allocation).  Return the HIP error
+// of the launch.
+hipError_t launch_quantize(const void* x, int64_t batch, int64_t rows, int64_t cols, int axis,
+                           int mode, uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+  if (batch == 0 || rows == 0 || cols == 0) return hipSuccess;
+  if (axis == 1 && (cols & 31) == 0) {
+    const int64_t nq = batch * rows * (cols / 32) * 4;
+    constexpr int U = 4;
+    int64_t grid = (nq + 256 * U - 1) / (256 * U);
+    if (grid > 8192) grid = 8192;
+    if (mode == kModeUOS)
+      quant_stream_kernel<kModeUOS, U><<<dim3(unsigned(grid)), dim3(256), 0, stream>>>(
+          static_cast<const uint4*>(x), reinterpret_cast<uint32_t*>(codes), scales, nq);
+    else
+      quant_stream_kernel<kModeOCP, U><<<dim3(unsigned(grid)), dim3(256), 0, stream>>>(
+          static_cast<const uint4*>(x), reinterpret_cast<uint32_t*>(codes), scales, nq);
+  } else if (axis == 1) {
+    const int64_t nb = (cols + 31) / 32;
+    const int64_t nblk = batch * rows * nb;
+    const int64_t grid = (nblk + 255) / 256;
+    if (mode == kModeUOS)
+      quant_rows_general_kernel<kModeUOS><<<dim3(unsigned(grid)), dim3(256), 0, stream>>>(
+          static_cast<const uint16_t*>(x), reinterpret_cast<uint4*>(codes), scales, batch * rows, cols, nb);
+    else
+      quant_rows_general_kernel<kModeOCP><<<dim3(unsigned(grid)), dim3(256), 0, stream>>>(
+          static_cast<const uint16_t*>(x), reinterpret_cast<uint4*>(codes), scales, batch * rows, cols, nb);
+  } else {
+    const int64_t nb = (rows + 31) / 32;
+    const int64_t ntr = (rows + 255) / 256, ntc = (cols + 63) / 64;
+    const dim3 grid(unsigned(ntr * ntc), unsigned(batch));
+    if (mode == kModeUOS)
+      quant_cols_kernel<kModeUOS><<<grid, dim3(256), 0, stream>>>(static_cast<const uint16_t*>(x),
+                                                                   codes, scales, rows, cols, nb, ntc);
+    else
+      quant_cols_kernel<kModeOCP><<<grid, dim3(256), 0, stream>>>(static_cast<const uint16_t*>(x),
+                                                                   codes, scales, rows, cols, nb, ntc);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mxattn
