@@ -1,0 +1,274 @@
+#!/usr/bin/env python3
+"""Benchmark of the MXFP4 attention hot path (MXAttention: UOS + PNQ) on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input that
+is already resident in HBM: quantize Q and K along d, quantize V along N, and
+run the fused MXFP4 attention kernel (exactly the launches mxattn_fwd makes,
+issued one by one so each kernel can be bracketed with HIP events on the
+stream it runs on).  Default workload: the Wan-style video DiT shape
+B=1, H=40, N=32760 (21 x 1560 tokens), d=128, UOS + PNQ, non-causal.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+
+    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--workload wan]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PEAK_FP4_TFLOPS = 10100.0  # MI355X dense MXFP4 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_wan_traffic.json")
+ATTN_SRC = os.path.join(ROOT, "mxfp4_quantized_attention_amd", "csrc", "attention.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def attn_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in ("attention.hip", "mx_device.h"):
+        with open(os.path.join(os.path.dirname(ATTN_SRC), name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary, or None when the counters were taken on another kernel version or
+    workload."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sha") != attn_source_hash() or t.get("workload") != workload:
+        return None
+    return float(t["bytes_per_launch"])
+
+
+def cpu_baseline(q, k, v, cfg, mode, pnq, kv_tile, gpu_out, heads=4, rows_per_head=1024):
+    """The oracle, timed on this host's cores on a bounded sample of the same
+    workload: K/V quantization of `heads` heads plus `rows_per_head` seeded
+    query rows of each."""
+    import numpy as np
+    import oracle
+    import workloads
+    B, H, N, d = q.shape
+    rows = []
+    g = np.random.default_rng(11)
+    for h in range(heads):
+        rows.append(h * N + np.sort(g.choice(N, rows_per_head, replace=False)))
+    rows = np.concatenate(rows)
+    qs, ks, vs = (x.reshape(B * H, N, d)[:heads] for x in (q, k, v))
+    t0 = time.perf_counter()
+    ref = oracle.attn_rows(qs, ks, vs, heads, N, d, mode, pnq, kv_tile, 1.0 / np.sqrt(d), rows)
+    dt = time.perf_counter() - t0
+    flop = 4.0 * N * d * rows.size
+    got = oracle.bf16_to_f64(gpu_out.reshape(B * H * N, d)[rows])
+    diff = np.abs(got - oracle.bf16_to_f64(ref["out_bf16"]))
+    return {
+        "value": flop / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"{cfg}: K/V quantization of {heads} heads + {rows.size} seeded query rows "
+                  f"({rows_per_head} per head), {dt:.1f} s; FLOP counted as 4*N*d per row",
+        "seconds": dt,
+        "max_abs_vs_gpu_on_sample": float(diff.max()),
+    }
+
+
+def quality_context(q, k, v, out_uos_pnq, out_ocp, nrows=64):
+    """Cosine and relative L2 against unquantized fp64 attention on sampled rows
+    (quality context only)."""
+    import numpy as np
+    import oracle
+    B, H, N, d = q.shape
+    g = np.random.default_rng(5)
+    res = {"rows": nrows}
+    cos = {"uos_pnq": [], "ocp": []}
+    for r in np.sort(g.choice(B * H * N, nrows, replace=False)):
+        h, i = divmod(int(r), N)
+        Q = oracle.bf16_to_f64(q.reshape(B * H, N, d)[h, i])
+        K = oracle.bf16_to_f64(k.reshape(B * H, N, d)[h])
+        V = oracle.bf16_to_f64(v.reshape(B * H, N, d)[h])
+        s = K @ Q / np.sqrt(d)
+        w = np.exp(s - s.max())
+        ref = (w @ V) / w.sum()
+        for name, o in (("uos_pnq", out_uos_pnq), ("ocp", out_ocp)):
+            x = oracle.bf16_to_f64(o.reshape(B * H, N, d)[h, i])
+            cos[name].append(float(x @ ref / np.sqrt((x @ x) * (ref @ ref))))
+    for name in cos:
+        res["mean_cos_" + name] = float(np.mean(cos[name]))
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="wan", choices=["tiny", "small", "wan", "hunyuan"])
+    ap.add_argument("--mode", default="uos", choices=["uos", "ocp"])
+    ap.add_argument("--no-pnq", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-quality", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one plain device-to-device copy of this many MiB before timing "
+                         "(reference for the rocprofv3 FETCH_SIZE/WRITE_SIZE scale factor)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the path shards by head with no communication, "
+              "and runs on more than one GPU are not part of this build", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import workloads
+    import mxfp4_quantized_attention_amd as mx
+
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    cfg = workloads.CONFIGS[args.workload]
+    B, H, N, d = cfg["B"], cfg["H"], cfg["N"], cfg["d"]
+    BH = B * H
+    mode = mx.MODE_UOS if args.mode == "uos" else mx.MODE_OCP
+    pnq = 0 if args.no_pnq else 1
+    log(f"[bench] generating {args.workload} inputs {B}x{H}x{N}x{d}")
+    t0 = time.perf_counter()
+    q, k, v = workloads.qkv(args.workload)
+    log(f"[bench] generated in {time.perf_counter() - t0:.1f} s; uploading")
+
+    def up(x):
+        return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    qg, kg, vg = up(q), up(k), up(v)
+    L = mx.lib()
+    nbn = (N + 31) // 32
+    u8 = dict(dtype=torch.uint8, device=dev)
+    qc, kc = torch.empty(BH * N * d // 2, **u8), torch.empty(BH * N * d // 2, **u8)
+    qs, ks = torch.empty(BH * N * d // 32, **u8), torch.empty(BH * N * d // 32, **u8)
+    vc, vs = torch.empty(BH * d * nbn * 16, **u8), torch.empty(BH * d * nbn, **u8)
+    o = torch.empty_like(qg)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    def launch_q():
+        return L.mxq_quantize(qg.data_ptr(), BH, N, d, 1, mode, qc.data_ptr(), qs.data_ptr(), sp)
+
+    def launch_k():
+        return L.mxq_quantize(kg.data_ptr(), BH, N, d, 1, mode, kc.data_ptr(), ks.data_ptr(), sp)
+
+    def launch_v():
+        return L.mxq_quantize(vg.data_ptr(), BH, N, d, 0, mode, vc.data_ptr(), vs.data_ptr(), sp)
+
+    def launch_attn():
+        return L.mxattn_fwd_quantized(qc.data_ptr(), qs.data_ptr(), kc.data_ptr(), ks.data_ptr(),
+                                      vc.data_ptr(), vs.data_ptr(), B, H, N, d, mode, pnq, 0.0,
+                                      o.data_ptr(), sp)
+
+    launches = (launch_q, launch_k, launch_v, launch_attn)
+
+    def step(ev=None):
+        for i, fn in enumerate(launches):
+            if ev is not None:
+                ev[i].record(stream)
+            st = fn()
+            if st != 0:
+                raise RuntimeError(f"launch {i} failed: {mx.status_string(st)}")
+        if ev is not None:
+            ev[len(launches)].record(stream)
+
+    if args.copy_calibration_mib:
+        nbytes = args.copy_calibration_mib << 20
+        src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {nbytes} bytes done")
+        del src, dst
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(launches) + 1)]
+              for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    per_kernel = np.array([[ev[i].elapsed_time(ev[i + 1]) for i in range(len(launches))] for ev in events])
+    kq, kk, kvv, ka = per_kernel.mean(axis=0)
+    flop = 4.0 * B * H * N * N * d
+    value = flop / (ms_per_step * 1e-3) / 1e12
+    achieved = flop / (ka * 1e-3) / 1e12
+    log(f"[bench] step {ms_per_step:.3f} ms -> {value:.1f} TFLOP/s; attention kernel {ka:.3f} ms "
+        f"-> {achieved:.1f} TFLOP/s; quantize Q {kq:.3f} K {kk:.3f} V {kvv:.3f} ms")
+
+    # the split launches are exactly mxattn_fwd: check bit-equality once
+    o_split = o.clone()
+    o_fwd = mx.fwd(qg, kg, vg, mode=args.mode, pnq=bool(pnq))
+    torch.cuda.synchronize()
+    same = bool(torch.equal(o_split.view(torch.int16), o_fwd.view(torch.int16)))
+    gpu_out = o_split.view(torch.int16).cpu().numpy().view(np.uint16)
+
+    qbytes = 2.53125 * BH * N * d
+    traffic = measured_traffic(args.workload)
+    result = {
+        "metric": "MXFP4 attention fwd TFLOP/s (4*B*H*N^2*d) and % of MI355X MXFP4 MFMA peak",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: B={B} H={H} N={N} d={d} non-causal, "
+                               f"{args.mode.upper()}{'+PNQ' if pnq else ''}",
+                   "B": B, "H": H, "N": N, "d": d, "mode": args.mode, "pnq": bool(pnq),
+                   "kv_tile": mx.kv_tile(d), "global_batch": B, "seq_len": N, "parallelism": "single GPU"},
+        "pct_of_fp4_peak": 100.0 * value / PEAK_FP4_TFLOPS,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_FP4_TFLOPS, "traffic": traffic,
+                     "kernel": "attn_fwd_kernel", "kernel_ms": ka,
+                     "algorithmic": f"4*d FLOP per score element x B*H*N^2 = {flop:.4g} FLOP per launch"},
+        "roofline_quantize": {"bound": "hbm", "unit": "GB/s", "peak": PEAK_HBM_GBS,
+                              "bytes_per_launch": qbytes,
+                              "q_axis1_ms": kq, "q_axis1_gbs": qbytes / (kq * 1e-3) / 1e9,
+                              "k_axis1_ms": kk, "k_axis1_gbs": qbytes / (kk * 1e-3) / 1e9,
+                              "v_axis0_ms": kvv, "v_axis0_gbs": qbytes / (kvv * 1e-3) / 1e9},
+        "step_equals_mxattn_fwd": same,
+    }
+    if not args.no_quality:
+        log("[bench] quality context")
+        o_ocp = mx.fwd(qg, kg, vg, mode="ocp", pnq=False)
+        torch.cuda.synchronize()
+        out_ocp = o_ocp.view(torch.int16).cpu().numpy().view(np.uint16)
+        result["quality"] = quality_context(q, k, v, gpu_out, out_ocp)
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(q, k, v, args.workload, mode, pnq, mx.kv_tile(d), gpu_out)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -55,7 +55,7 @@ WsLayout ws_layout(int64_t BH, int64_t N, int64_t d) {
 int check_attn_sizes(int64_t B, int64_t H, int64_t N, int64_t d) {
   if (B < 1 || H < 1 || N < 1) return MXQ_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return MXQ_ERR_UNSUPPORTED;
-  if (B > (int64_t(1) << 20) || H > (int64_t(1) << 20) || N > (int64_t(1) << 26)) return MXQ_ERR_UNSUPPORTED;
+  if (B > (int64_t(1) << 20) || H > (int64_t(1) << 20) || N > (int64_t(1) << 24)) return MXQ_ERR_UNSUPPORTED;
   const int64_t BH = B * H;
   if (BH > (int64_t(1) << 24) || BH * N * d > kMaxAttnElems) return MXQ_ERR_UNSUPPORTED;
   // the workgroup count (BH * ceil(N / 256), rounded to 8) must fit an int

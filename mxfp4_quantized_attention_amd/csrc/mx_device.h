@@ -58,13 +58,13 @@ __device__ __forceinline__ uint32_t cvt_fp4x2(uint32_t old, float a, float b, fl
 // A (16 rows x 128 K): lane l holds row l%16, K = 32*(l/16) + [0, 32) as 32
 // nibbles in a[0..3] (nibble n of the 128 bits = K offset n).  B (128 K x 16
 // cols): lane l holds col l%16 with the same K slice.  C/D: lane l holds col
-// l%16, rows 4*(l/16) + [0, 4).  sa/sb: the E8M0 scale byte of the lane's
-// 32-element K slice (byte 0 of the register).
-__device__ __forceinline__ v4f mfma_fp4_16x16x128(const uint4& a, const uint4& b, v4f c,
-                                                    int sa, int sb) {
+// l%16, rows 4*(l/16) + [0, 4).  sa/sb: registers holding the E8M0 scale of the
+// lane's 32-element K slice in byte SA/SB.
+template <int SA = 0, int SB = 0>
+__device__ __forceinline__ v4f mfma_fp4_16x16x128(const uint4& a, const uint4& b, v4f c, int sa, int sb) {
   v8i A = {int(a.x), int(a.y), int(a.z), int(a.w), 0, 0, 0, 0};
   v8i B = {int(b.x), int(b.y), int(b.z), int(b.w), 0, 0, 0, 0};
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, c, 4, 4, 0, sa, 0, sb);
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, c, 4, 4, SA, sa, SB, sb);
 }
 
 }  // namespace mxattn

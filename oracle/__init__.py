@@ -80,6 +80,8 @@ def _load():
     lib.orc_attn_rows.restype = i32
     lib.orc_dump.argtypes = [ctypes.c_char_p, P, P, i64, i64, i64, i32, i32]
     lib.orc_dump.restype = i32
+    lib.orc_num_threads.argtypes = []
+    lib.orc_num_threads.restype = i32
     _lib = lib
     return lib
 
@@ -90,6 +92,11 @@ def _ptr(a: np.ndarray | None):
 
 def _c(a, dtype):
     return np.ascontiguousarray(a, dtype=dtype)
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's row loop runs on."""
+    return int(_load().orc_num_threads())
 
 
 def bf16_to_f64(bits) -> np.ndarray:

@@ -302,20 +302,38 @@ static double scale_boundary_distance(double amax, int mode)
 }
 
 /* Quantize one P block held in fp32-rounded doubles p[0..n) (n <= 32, the
- * rest of the 32-key block is padding) into p_hat; returns 1 when a decision
- * lies within 2^-20 (relative) of a tie or of a scale boundary. */
-static int quant_p_block(const double *p, int n, int mode, double *p_hat)
+ * rest of the 32-key block is padding) into p_hat.  Returns 1 when one of the
+ * block's decisions (its scale, or an element's code) lies so close to a
+ * boundary that the fp32 definition of p does not settle it.
+ *
+ * The exponential is defined from fp32 scores t (t = fp32(s * scale)) and the
+ * running max m, so p itself is only fixed to about 2^-24 (|t| + |m|)
+ * relative: any fp32 evaluation order moves it by that much.  A decision is
+ * flagged when it lies within eps = 2^-22 (4 + |t| + |m|) of a tie (relative),
+ * which covers the roundings of t, m, the scale product and the exponential.
+ * Blocks whose largest exponential is below 2^-60 are never flagged: their
+ * weights cannot reach any output at the acceptance tolerance.  An amax of
+ * exactly 1 (the block holding the running max) is exact on every side. */
+static int quant_p_block(const double *p, const double *t, double m, int n, int mode,
+                         double *p_hat)
 {
-    double amax = 0.0;
-    for (int i = 0; i < n; ++i)
+    double amax = 0.0, tmax = -INFINITY;
+    for (int i = 0; i < n; ++i) {
         if (p[i] > amax)
             amax = p[i];
+        if (t[i] > tmax)
+            tmax = t[i];
+    }
     int e = orc_block_exponent(amax, mode);
-    int near = scale_boundary_distance(amax, mode) < 0x1p-20;
+    int near = 0;
+    const int relevant = amax >= 0x1p-60;
+    if (relevant && amax != 1.0 &&
+        scale_boundary_distance(amax, mode) < 0x1p-22 * (4.0 + fabs(tmax) + fabs(m)))
+        near = 1;
     for (int i = 0; i < n; ++i) {
         double y = ldexp(p[i], -e);
         p_hat[i] = orc_e2m1_value(orc_e2m1_encode(y), e);
-        if (y > 0.0 && e2m1_tie_distance(y) < 0x1p-20)
+        if (relevant && y > 0.0 && e2m1_tie_distance(y) < 0x1p-22 * (4.0 + fabs(t[i]) + fabs(m)))
             near = 1;
     }
     return near;
@@ -329,7 +347,8 @@ static int quant_p_block(const double *p, int n, int mode, double *p_hat)
  * query row (head = rows[i] / N).  Outputs per requested row:
  *   out[i*d + c]   O = (sum_k w_k v_k) in fp64 (before bf16 rounding),
  *   lsum[i]        the final row sum l (may be NULL),
- *   flags[i]       bit 0: a P decision was within 2^-20 of a tie (may be NULL),
+ *   flags[i]       bit 0: a P decision lay within the fp32 resolution of p
+ *                  of a tie (see quant_p_block; may be NULL),
  *   weights[i*N+k] explicit weights w_k with O = sum_k w_k * deq(v_k)
  *                  (may be NULL; costs O(N^2 / Bc) per row).
  *
@@ -463,7 +482,7 @@ int orc_attn_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v, int64
                 } else {
                     for (int64_t b0 = t0; b0 < t1; b0 += 32) {
                         int n = (int)(t1 - b0 < 32 ? t1 - b0 : 32);
-                        near |= quant_p_block(p + b0, n, mode, ph + b0);
+                        near |= quant_p_block(p + b0, t + b0, mnew, n, mode, ph + b0);
                     }
                 }
                 double rs = 0.0;
@@ -552,4 +571,17 @@ void orc_block_exponent_array(const double *amax, int64_t n, int mode, int32_t *
 {
     for (int64_t i = 0; i < n; ++i)
         e[i] = orc_block_exponent(amax[i], mode);
+}
+
+/* Number of OpenMP threads the row loop uses. */
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+int orc_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
 }

@@ -43,8 +43,10 @@ def compare_attention(gpu_bits, ref, near_tie=None, atol=2e-3, rel_l2_max=1e-3, 
     compared with the GPU's bf16 output: relative L2 <= rel_l2_max over all
     checked elements, and per element |diff| <= max(atol, one bf16 ulp of the
     reference).  Rows the oracle flags as holding a quantization decision
-    within 2^-20 of a tie may differ beyond the per-element bound (either
-    rounding is correct there); they still count in the relative L2."""
+    that the fp32 definition of the exponentials does not settle (within
+    2^-22 (4 + |t| + |m|) of a tie) may differ beyond the per-element bound
+    (either rounding is correct there); they still count in the relative L2,
+    and at most 1% of the rows (plus one) may exceed the per-element bound."""
     g = oracle.bf16_to_f64(gpu_bits).reshape(ref["out"].shape)
     r = oracle.bf16_to_f64(ref["out_bf16"]).reshape(ref["out"].shape)
     diff = np.abs(g - r)
@@ -57,5 +59,7 @@ def compare_attention(gpu_bits, ref, near_tie=None, atol=2e-3, rel_l2_max=1e-3, 
                 flagged_rows=int(np.sum(flagged)), unexplained=unexplained[:10])
     print(what, info)
     assert not unexplained, f"{what}: rows beyond tolerance that the oracle did not flag: {info}"
+    n = len(flagged)
+    assert len(bad_rows) <= 1 + n // 100, f"{what}: too many rows beyond tolerance: {info}"
     assert rel <= rel_l2_max, f"{what}: relative L2 {rel} > {rel_l2_max}"
     return info

@@ -2,7 +2,8 @@
 
 Acceptance: the oracle's output rounded to bf16 vs the GPU's bf16 output,
 relative L2 <= 1e-3 and per element |diff| <= max(2e-3, 1 bf16 ulp), with
-rows holding a quantization decision within 2^-20 of a tie exempt from the
+rows holding a quantization decision the fp32 definition of p does not settle
+(the oracle flags them: within 2^-22 (4 + |t| + |m|) of a tie) exempt from the
 per-element bound (either rounding is correct there).  Small workloads are
 checked in full, the large ones on 512 seeded sampled query rows (rows are
 independent, so sampling is exact).
