@@ -5,21 +5,20 @@
 // i.e. the unnormalized exponentials exp(s - m) are quantized to MXFP4 before
 // they are summed, so the row sum and P.V see the same values.
 //
-// Kernel structure (one workgroup = 128 queries of one head, 4 waves of 32
-// queries = two 16-query groups per wave; two workgroups share a CU so their
-// MFMA and VALU phases interleave on each SIMD):
-//   K/V tiles of kBC = 128 keys, double-buffered in LDS (the next tile is
-//   fetched into registers while the current one is used; one barrier per
-//   tile).  For each tile, in ascending key order:
+// Kernel structure: one workgroup = 128 queries of one head, 8 waves of one
+// 16-query group each; two workgroups share a CU, so every SIMD holds four
+// waves (at most 128 VGPRs each) and hides one wave's latency with the
+// others' work.
+//   K/V tiles of kBC = 128 keys, double-buffered in LDS: the next tile streams
+//   from global memory straight into LDS while the current one is used, and
+//   one barrier per tile publishes it.  For each tile, in ascending key order:
 //     S^T = K Q^T with one 16x16x128 FP4 MFMA per 16 keys (Q stays in
 //       registers as the B operand; the E8M0 scales go in as MFMA scales);
-//     per 16-query group: running max, alpha = exp(m_old - m_new);
+//     running max per query, alpha = exp(m_old - m_new);
 //     p = exp(s - m_new) in fp32, quantized per 32-key block in registers;
 //     l = alpha l + sum(p_q)   (PNQ: one extra MFMA against a ones tile)
 //       or alpha l + sum(p)    (PNQ off);
 //     O^T = alpha O^T + V^T P_q^T, one 16x16x128 MFMA per 16 channels.
-//     The second group's S^T MFMAs run under the first group's softmax VALU
-//     work, and the first group's P.V MFMAs under the second group's.
 //   O = O / l rounded to bf16.
 //
 // The K rows fed to the S^T MFMA are permuted so that every lane's 32 output
@@ -27,6 +26,8 @@
 // and keys 32*(l/16) + [0, 32) of the tile.  Block maxima and the FP4 encode
 // then stay inside the lane, and the packed codes are already the lane's B
 // operand slice (query l%16, keys 32*(l/16) + n) of the P.V MFMA.
+#include <type_traits>
+
 #include "mx_device.h"
 
 namespace mxattn {
@@ -48,8 +49,8 @@ struct AttnArgs {
 };
 
 constexpr int kBC = 128;    // keys per tile: the running-max update granularity
-constexpr int kWaves = 4;   // waves per workgroup (two workgroups share a CU)
-constexpr int kQG = 2;      // 16-query groups per wave
+constexpr int kWaves = 8;   // waves per workgroup (two workgroups share a CU)
+constexpr int kQG = 1;      // 16-query groups per wave
 constexpr int kBR = kWaves * kQG * 16;  // queries per workgroup
 
 namespace {
@@ -84,17 +85,24 @@ __device__ __forceinline__ float sum_over_blocks(float x) {
 
 // LDS layout of one 128-key tile.  K codes [key][64 B] and V codes
 // [channel][64 B] (the tile's four 32-key blocks), 16-byte chunks XOR-swizzled
-// so the 16 rows read by one MFMA operand load land in distinct bank groups.
+// so the rows read by one MFMA operand load hit distinct banks, whether the LDS
+// serves 8 lanes from 32 banks or 16 lanes from 64 banks per cycle; the
+// swizzle term of a lane does not change from one sub-tile to the next.
 // Scales are stored in MFMA lane order, 8 bytes per lane: ks[lane][t] is the
 // K scale of sub-tile t (key row of that lane in sub-tile t, d-block l/16),
 // vs[lane][ct] the V scale of channel tile ct (channel 16 ct + l%16, block
 // l/16); one 8-byte read per lane fetches all of them and the MFMA's op_sel
 // picks the byte.
-__device__ __forceinline__ int k_chunk_addr(int row, int c) { return row * 64 + 16 * (c ^ ((row >> 5) & 3)); }
-__device__ __forceinline__ int v_chunk_addr(int row, int c) { return row * 64 + 16 * (c ^ ((row >> 2) & 3)); }
+__device__ __forceinline__ int k_swz(int row) { return ((row >> 5) & 3) ^ (row & 2); }
+__device__ __forceinline__ int v_swz(int row) { return ((row >> 2) & 3) ^ (row & 2); }
+__device__ __forceinline__ int k_chunk_addr(int row, int c) { return row * 64 + 16 * (c ^ k_swz(row)); }
+__device__ __forceinline__ int v_chunk_addr(int row, int c) { return row * 64 + 16 * (c ^ v_swz(row)); }
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
-typedef __attribute__((address_space(1))) void* glb_ptr;
+
+// Word 3 of a raw buffer descriptor on gfx9-class GPUs (32-bit data format,
+// no swizzle): offsets at or past the record count read as zero.
+constexpr int kBufferFlags = 0x00020000;
 
 struct __align__(16) TileLds {
   uint8_t k[kBC * 64];
@@ -133,35 +141,31 @@ __device__ __forceinline__ void softmax_group(v4f (&S)[8], float& m, float c, ui
   e = e < -126 ? -126 : e;
   pS = e + 127;
   const float sc = pow2f(e);
-  float p[8][4];
-#pragma unroll
-  for (int t = 0; t < 8; ++t)
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) p[t][jj] = fast_exp2(fmaf(S[t][jj], c, -mc));
-  // nibble n of the operand = key 32*g4 + n, n = 4t + jj
+  // exponentials and their FP4 codes, one 8-code dword at a time (nibble n
+  // of the operand = key 32*g4 + n, n = 4t + jj)
   uint32_t d[4];
+  float ps = 0.f;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
+    float p[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[i] = fast_exp2(fmaf(S[2 * w + i / 4][i % 4], c, -mc));
     uint32_t x = 0;
-    x = cvt_fp4x2<0>(x, p[2 * w][0], p[2 * w][1], sc);
-    x = cvt_fp4x2<1>(x, p[2 * w][2], p[2 * w][3], sc);
-    x = cvt_fp4x2<2>(x, p[2 * w + 1][0], p[2 * w + 1][1], sc);
-    x = cvt_fp4x2<3>(x, p[2 * w + 1][2], p[2 * w + 1][3], sc);
+    x = cvt_fp4x2<0>(x, p[0], p[1], sc);
+    x = cvt_fp4x2<1>(x, p[2], p[3], sc);
+    x = cvt_fp4x2<2>(x, p[4], p[5], sc);
+    x = cvt_fp4x2<3>(x, p[6], p[7], sc);
     d[w] = x;
+    if (!PNQ) ps += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
   }
   pk = make_uint4(d[0], d[1], d[2], d[3]);
-  if (!PNQ) {
-    float ps = 0.f;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) ps += (p[t][0] + p[t][1]) + (p[t][2] + p[t][3]);
-    lpart = lpart * alpha + ps;
-  }
+  if (!PNQ) lpart = lpart * alpha + ps;
 }
 
 }  // namespace
 
 template <int D, int MODE, bool PNQ>
-__global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void attn_fwd_kernel(AttnArgs a) {
   constexpr int DB = D / 32;      // 32-blocks along d in a Q/K row
   constexpr int CROW = D / 2;     // code bytes per Q/K row
   constexpr int NCT = D / 16;     // 16-channel tiles of O^T
@@ -169,7 +173,9 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_kernel(AttnArgs a) {
   constexpr int KI = kBC * 4 / 64;  // wave-wide 16-byte fills per K tile
   constexpr int VI = D * 4 / 64;    // wave-wide 16-byte fills per V tile
   static_assert(kBC + D <= NT, "one scale word per thread");
-  static_assert(KI % kWaves == 0 && VI % kWaves == 0, "fills split evenly over the waves");
+  static_assert(KI % kWaves == 0 || kWaves % KI == 0, "fills split evenly over the waves");
+  static_assert(VI % kWaves == 0 || kWaves % VI == 0, "fills split evenly over the waves");
+  constexpr int KU = (KI + kWaves - 1) / kWaves, VU = (VI + kWaves - 1) / kWaves;  // fills per wave
   __shared__ TileLds lds0, lds1;
 
   // Tile order: workgroup w is dispatched to XCD w % 8.  Each XCD gets a
@@ -191,7 +197,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_kernel(AttnArgs a) {
   int qS[kQG];
 #pragma unroll
   for (int g = 0; g < kQG; ++g) {
-    const int qi = qt * kBR + wave * 32 + g * 16 + r16;
+    const int qi = qt * kBR + wave * (kQG * 16) + g * 16 + r16;
     qB[g] = make_uint4(0, 0, 0, 0);
     qS[g] = 127;
     if (qi < N && g4 < DB) {
@@ -217,8 +223,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_kernel(AttnArgs a) {
   // Per-lane LDS offsets.  Sub-tile t of the K operand is k_lane + 256 t (the
   // swizzle term does not depend on t); channel tile ct of the V operand is
   // v_lane + 1024 ct; this lane's 8 scale bytes sit at s_lane.
-  const int k_lane = (32 * (r16 >> 2) + (r16 & 3)) * 64 + 16 * (g4 ^ (r16 >> 2));
-  const int v_lane = r16 * 64 + 16 * (g4 ^ (r16 >> 2));
+  const int k_lane = (32 * (r16 >> 2) + (r16 & 3)) * 64 + 16 * (g4 ^ (r16 >> 2) ^ (r16 & 2));
+  const int v_lane = r16 * 64 + 16 * (g4 ^ (r16 >> 2) ^ (r16 & 2));
   const int s_lane = lane * 8;
 
   const int ntk = (N + kBC - 1) / kBC;
@@ -227,58 +233,63 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_kernel(AttnArgs a) {
   const uint8_t* vc_h = a.vc + bh * int64_t(D) * nbn * 16;
   const uint8_t* vs_h = a.vs + bh * int64_t(D) * nbn;
 
-  // Tile fetch.  Code chunks go straight from global memory into LDS
-  // (global_load_lds_dwordx4: lane i of a wave writes the 16 bytes at
-  // dst + 16 i), so the swizzle is applied on the source side: LDS slot s of
-  // the K tile holds (row s/4, chunk (s%4) ^ swizzle(row)).  In the last tile,
-  // rows past N and V blocks past the padded end read the last valid row or
-  // block instead (finite data whose scores are masked to -inf or whose
-  // weights are 0).  Scale bytes take a register detour (one VGPR).
-  int koff[KI / kWaves], krow_[KI / kWaves], kcol_[KI / kWaves];
+  // Tile fetch.  Code chunks go straight from global memory into LDS (lane i
+  // of a wave writes the 16 bytes at dst + 16 i), so the swizzle is applied on
+  // the source side: LDS slot s of the K tile holds (row s/4, chunk
+  // (s%4) ^ swizzle(row)).  Scale bytes take a register detour (one VGPR).
+  // Per-thread fill offsets (bytes from the tile's base in global memory).
+  int koff[KU], voff[VU];
 #pragma unroll
-  for (int u = 0; u < KI / kWaves; ++u) {
+  for (int u = 0; u < KU; ++u) {
     const int slot = (wave + u * kWaves) * 64 + lane;
     const int row = slot >> 2;
-    krow_[u] = row;
-    kcol_[u] = ((slot & 3) ^ ((row >> 5) & 3)) % (CROW / 16);
-    koff[u] = row * CROW + 16 * kcol_[u];
+    koff[u] = row * CROW + 16 * (((slot & 3) ^ k_swz(row)) % (CROW / 16));
   }
-  int voff[VI / kWaves], vrow_[VI / kWaves], vblk_[VI / kWaves];
 #pragma unroll
-  for (int u = 0; u < VI / kWaves; ++u) {
+  for (int u = 0; u < VU; ++u) {
     const int slot = (wave + u * kWaves) * 64 + lane;
     const int row = slot >> 2;
-    vrow_[u] = row;
-    vblk_[u] = (slot & 3) ^ ((row >> 2) & 3);
-    voff[u] = (row * nbn + vblk_[u]) * 16;
+    voff[u] = (row * nbn + ((slot & 3) ^ v_swz(row))) * 16;
   }
-  // where this thread's scale bytes go in the lane-ordered layout
-  const int sk_key = tid;                   // tid < kBC: key of the tile
-  const int sk_t = (sk_key & 31) >> 2, sk_r = ((sk_key >> 5) << 2) | (sk_key & 3);
-  const int sv_ch = tid - kBC;              // kBC <= tid < kBC + D: channel
-  const int sv_ct = sv_ch >> 4, sv_r = sv_ch & 15;
+  // Where this thread's scale bytes go in the lane-ordered layout: byte b of
+  // key tid (tid < kBC) to ks[(16 b + r) * 8 + t], byte b of channel tid - kBC
+  // to vs[(16 b + r) * 8 + ct]; vs follows ks, so one offset from ks serves both.
+  int sdst = 0, snb = 0;
+  if (tid < kBC) {
+    sdst = ((((tid >> 5) << 2) | (tid & 3)) * 8) + ((tid & 31) >> 2);
+    snb = DB;
+  } else if (tid < kBC + D) {
+    const int ch = tid - kBC;
+    sdst = 64 * 8 + (ch & 15) * 8 + (ch >> 4);
+    snb = 4;
+  }
 
   uint32_t sreg = 0;
+  // Code fills use raw buffer loads into LDS: the descriptor's base is the
+  // tile's first byte and its record count the bytes left in the head, so the
+  // hardware range check returns zeros for K rows past N.  V blocks past the
+  // padded end read the next channel's finite data (weight 0) or zeros.
+  const int64_t khead = int64_t(N) * CROW, vhead = int64_t(D) * nbn * 16;
   auto issue_tile = [&](int j, TileLds& T) {
     const int kb = j * kBC;
     const int vb0 = kb / 32;
-    const bool full_k = kb + kBC <= N;
-    const bool full_v = vb0 + 4 <= nbn;
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kc_h + int64_t(kb) * CROW), 0, int(khead - int64_t(kb) * CROW), kBufferFlags);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(vc_h + int64_t(vb0) * 16), 0, int(vhead - int64_t(vb0) * 16), kBufferFlags);
 #pragma unroll
-    for (int u = 0; u < KI / kWaves; ++u) {
-      const uint8_t* src = full_k ? kc_h + int64_t(kb) * CROW + koff[u]
-                                  : kc_h + int64_t(min(kb + krow_[u], N - 1)) * CROW + 16 * kcol_[u];
-      __builtin_amdgcn_global_load_lds((glb_ptr)src, (lds_ptr)(T.k + (wave + u * kWaves) * 1024), 16, 0, 0);
-    }
+    for (int u = 0; u < KU; ++u)
+      if (KI % kWaves == 0 || wave + u * kWaves < KI)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr)(T.k + (wave + u * kWaves) * 1024), 16,
+                                                 uint32_t(koff[u]), 0, 0, 0);
 #pragma unroll
-    for (int u = 0; u < VI / kWaves; ++u) {
-      const uint8_t* src = full_v ? vc_h + int64_t(vb0) * 16 + voff[u]
-                                  : vc_h + (int64_t(vrow_[u]) * nbn + min(vb0 + vblk_[u], nbn - 1)) * 16;
-      __builtin_amdgcn_global_load_lds((glb_ptr)src, (lds_ptr)(T.v + (wave + u * kWaves) * 1024), 16, 0, 0);
-    }
+    for (int u = 0; u < VU; ++u)
+      if (VI % kWaves == 0 || wave + u * kWaves < VI)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr)(T.v + (wave + u * kWaves) * 1024), 16,
+                                                 uint32_t(voff[u]), 0, 0, 0);
     sreg = 0;
     if (tid < kBC) {
-      const uint8_t* p = ks_h + int64_t(min(kb + sk_key, N - 1)) * DB;
+      const uint8_t* p = ks_h + int64_t(min(kb + tid, N - 1)) * DB;
       if (DB == 4) {
         sreg = *reinterpret_cast<const uint32_t*>(p);
       } else {
@@ -286,102 +297,109 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_kernel(AttnArgs a) {
         for (int b = 0; b < DB; ++b) sreg |= uint32_t(p[b]) << (8 * b);
       }
     } else if (tid < kBC + D) {
-      const uint8_t* p = vs_h + int64_t(sv_ch) * nbn;
+      const uint8_t* p = vs_h + int64_t(tid - kBC) * nbn;
 #pragma unroll
       for (int b = 0; b < 4; ++b) sreg |= uint32_t(p[min(vb0 + b, nbn - 1)]) << (8 * b);
     }
   };
   auto finish_tile = [&](TileLds& T) {
-    if (tid < kBC) {
 #pragma unroll
-      for (int b = 0; b < DB; ++b) T.ks[(b * 16 + sk_r) * 8 + sk_t] = uint8_t(sreg >> (8 * b));
-    } else if (tid < kBC + D) {
-#pragma unroll
-      for (int b = 0; b < 4; ++b) T.vs[(b * 16 + sv_r) * 8 + sv_ct] = uint8_t(sreg >> (8 * b));
-    }
+    for (int b = 0; b < 4; ++b)
+      if (b < snb) T.ks[sdst + 128 * b] = uint8_t(sreg >> (8 * b));
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's LDS fills have landed
   };
 
-  auto compute_tile = [&](int j, const TileLds& T) {
+  // ---- one key tile: S^T, softmax step, l and O^T updates for every group ----
+  auto compute_tile = [&](auto masked, int j, const TileLds& T) {
+    constexpr bool MASKED = decltype(masked)::value;
     const int kb = j * kBC;
-    // ---- S^T = K Q^T for both groups: 8 MFMAs of 16 keys each ----
     uint2 ksw = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
     if (g4 < DB) ksw = *reinterpret_cast<const uint2*>(&T.ks[s_lane]);
     v4f S[kQG][8];
-#define MXATTN_S_STEP(t_)                                                                       \
-    {                                                                                           \
-      const uint4 kA = *reinterpret_cast<const uint4*>(&T.k[k_lane + 256 * (t_)]);              \
-      _Pragma("unroll") for (int g = 0; g < kQG; ++g) S[g][t_] =                                \
-          mfma_fp4_16x16x128<(t_) & 3, 0>(kA, qB[g], v4f{0.f, 0.f, 0.f, 0.f},                   \
-                                          int((t_) < 4 ? ksw.x : ksw.y), qS[g]);                 \
+#define MXATTN_S_STEP(t_)                                                                     \
+    {                                                                                         \
+      const uint4 kA = *reinterpret_cast<const uint4*>(&T.k[k_lane + 256 * (t_)]);            \
+      _Pragma("unroll") for (int g = 0; g < kQG; ++g) S[g][t_] =                              \
+          mfma_fp4_16x16x128<(t_) & 3, 0>(kA, qB[g], v4f{0.f, 0.f, 0.f, 0.f},                 \
+                                          int((t_) < 4 ? ksw.x : ksw.y), qS[g]);               \
     }
     MXATTN_S_STEP(0) MXATTN_S_STEP(1) MXATTN_S_STEP(2) MXATTN_S_STEP(3)
     MXATTN_S_STEP(4) MXATTN_S_STEP(5) MXATTN_S_STEP(6) MXATTN_S_STEP(7)
 #undef MXATTN_S_STEP
-    // keys past N (last tile only): s = -inf, so p = 0
-    if (kb + kBC > N) {
+    if constexpr (MASKED) {
+      // keys past N (the last tile only): s = -inf, so p = 0
+      if (kb + kBC > N) {
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
+        for (int t = 0; t < 8; ++t)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-          if (kb + 32 * g4 + 4 * t + jj >= N) {
+          for (int jj = 0; jj < 4; ++jj)
+            if (kb + 32 * g4 + 4 * t + jj >= N) {
 #pragma unroll
-            for (int g = 0; g < kQG; ++g) S[g][t][jj] = -INFINITY;
-          }
+              for (int g = 0; g < kQG; ++g) S[g][t][jj] = -INFINITY;
+            }
+      }
     }
-    // ---- softmax step per group (rescaling O and l when a running max moved) ----
     uint4 pk[kQG];
     int pS[kQG];
 #pragma unroll
     for (int g = 0; g < kQG; ++g) {
       float alpha;
       softmax_group<MODE, PNQ>(S[g], m[g], c, pk[g], pS[g], alpha, lpart[g]);
-      if (__any(alpha != 1.0f)) {
+      if (__any(alpha != 1.0f)) {  // rescale only when some running max moved
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) O[g][ct] *= alpha;
         if (PNQ) L[g] *= alpha;
       }
     }
-    // ---- l += sum(p_q) (PNQ) and O^T += V^T P_q^T, each V operand feeding both groups ----
     if (PNQ) {
 #pragma unroll
       for (int g = 0; g < kQG; ++g) L[g] = mfma_fp4_16x16x128(ones, pk[g], L[g], 127, pS[g]);
     }
     const uint2 vsw = *reinterpret_cast<const uint2*>(&T.vs[s_lane]);
-#define MXATTN_PV_STEP(ct_)                                                                     \
-    if ((ct_) < NCT) {                                                                          \
-      const uint4 vA = *reinterpret_cast<const uint4*>(&T.v[v_lane + 1024 * (ct_)]);            \
-      _Pragma("unroll") for (int g = 0; g < kQG; ++g) O[g][(ct_) % NCT] =                       \
-          mfma_fp4_16x16x128<(ct_) & 3, 0>(vA, pk[g], O[g][(ct_) % NCT],                        \
-                                           int((ct_) < 4 ? vsw.x : vsw.y), pS[g]);               \
+#define MXATTN_PV_STEP(ct_)                                                                   \
+    if ((ct_) < NCT) {                                                                        \
+      const uint4 vA = *reinterpret_cast<const uint4*>(&T.v[v_lane + 1024 * (ct_)]);          \
+      _Pragma("unroll") for (int g = 0; g < kQG; ++g) O[g][(ct_) % NCT] =                     \
+          mfma_fp4_16x16x128<(ct_) & 3, 0>(vA, pk[g], O[g][(ct_) % NCT],                      \
+                                           int((ct_) < 4 ? vsw.x : vsw.y), pS[g]);             \
     }
     MXATTN_PV_STEP(0) MXATTN_PV_STEP(1) MXATTN_PV_STEP(2) MXATTN_PV_STEP(3)
     MXATTN_PV_STEP(4) MXATTN_PV_STEP(5) MXATTN_PV_STEP(6) MXATTN_PV_STEP(7)
 #undef MXATTN_PV_STEP
   };
 
-  // Two LDS buffers; the loop is unrolled by two so each half addresses a
-  // fixed buffer (constant LDS offsets).
-  auto step = [&](int j, const TileLds& cur, TileLds& nxt) {
-    if (j + 1 < ntk) issue_tile(j + 1, nxt);  // lands during this tile's compute
-    compute_tile(j, cur);
-    if (j + 1 < ntk) finish_tile(nxt);
-    __syncthreads();
+  // ---- tile loop over two LDS buffers ----
+  // Tile j+1 streams into the other buffer while tile j is used; one barrier
+  // per tile publishes it (and frees the buffer just read).  Unrolled by two
+  // so every buffer address is a constant; the last one or two tiles run the
+  // variant that masks keys past N (a no-op unless the tile is ragged).
+  const std::integral_constant<bool, false> full_tile;
+  const std::integral_constant<bool, true> ragged_tile;
+  auto step = [&](auto masked, int j, const TileLds& cur, TileLds& nxt) {
+    if (j + 1 < ntk) issue_tile(j + 1, nxt);
+    compute_tile(masked, j, cur);
+    if (j + 1 < ntk) {
+      finish_tile(nxt);
+      __syncthreads();
+    }
   };
   issue_tile(0, lds0);
   finish_tile(lds0);
   __syncthreads();
-  for (int j = 0; j < ntk; j += 2) {
-    step(j, lds0, lds1);
-    if (j + 1 < ntk) step(j + 1, lds1, lds0);
+  int j = 0;
+  for (; j + 2 < ntk; j += 2) {
+    step(full_tile, j, lds0, lds1);
+    step(full_tile, j + 1, lds1, lds0);
   }
+  step(ragged_tile, j, lds0, lds1);
+  if (j + 1 < ntk) step(ragged_tile, j + 1, lds1, lds0);
 
   // ---- epilogue: O / l -> bf16 ----
 #pragma unroll
   for (int g = 0; g < kQG; ++g) {
     const float l = PNQ ? L[g][0] : sum_over_blocks(lpart[g]);
     const float inv = 1.0f / l;
-    const int qi = qt * kBR + wave * 32 + g * 16 + r16;
+    const int qi = qt * kBR + wave * (kQG * 16) + g * 16 + r16;
     if (qi < N) {
       uint16_t* orow = a.o + (bh * N + qi) * int64_t(D);
 #pragma unroll
