@@ -191,12 +191,18 @@ def main():
             ev[len(launches)].record(stream)
 
     if args.copy_calibration_mib:
+        # a plain elementwise copy kernel of known size (reads and writes
+        # nbytes each): the reference that scales rocprofv3's FETCH_SIZE and
+        # WRITE_SIZE counters to bytes
         nbytes = args.copy_calibration_mib << 20
-        src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
-        dst.copy_(src)
+        flush = torch.ones(2 * nbytes // 4, dtype=torch.float32, device=dev)  # evict src from the caches
+        del flush
         torch.cuda.synchronize()
-        log(f"[bench] calibration copy of {nbytes} bytes done")
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy kernel: {nbytes} bytes read, {nbytes} bytes written")
         del src, dst
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
