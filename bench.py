@@ -54,7 +54,7 @@ def measured_traffic(workload: str):
     return float(t["bytes_per_launch"])
 
 
-def cpu_baseline(q, k, v, cfg, mode, pnq, kv_tile, gpu_out, heads=4, rows_per_head=1024):
+def cpu_baseline(q, k, v, cfg, mode, pnq, kv_tile, gpu_out, heads=8, rows_per_head=2048):
     """The oracle, timed on this host's cores on a bounded sample of the same
     workload: K/V quantization of `heads` heads plus `rows_per_head` seeded
     query rows of each."""

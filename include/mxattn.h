@@ -91,7 +91,7 @@ int mxq_quantize(const void *x_bf16, int64_t batch, int64_t rows, int64_t cols, 
  * updated once per key tile, in ascending key order, and the quantized
  * exponentials are formed against that running maximum; the key tile is
  * therefore part of the definition of the result (the abstract only speaks of
- * "the softmax loop"; this is the flash-attention reading).
+ * the online softmax; this is the flash-attention reading).
  */
 int mxattn_kv_tile(int64_t d);
 

@@ -18,6 +18,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmxattn.so")
 SOURCES = ["abi.hip", "quantize.hip", "attention.hip"]
+# The attention kernel never sees a NaN (inputs are finite by contract and the
+# running max starts at -inf, never inf - inf); without NaNs the compiler drops
+# the canonicalizing moves it otherwise puts in front of every fmaxf.
+PER_FILE_FLAGS = {"attention.hip": ["-fno-honor-nans"]}
 ARCH = "gfx950"
 
 
@@ -40,7 +44,7 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(src):
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
-        cmd = [hipcc(), *flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc(), *flags(), *PER_FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                          if "packed-fp32-ops" not in l)

@@ -1,7 +1,7 @@
 // attention.hip -- fused non-causal MXFP4 attention forward for gfx950.
 //
 // MXAttention (arXiv 2607.24377), abstract: Q.K^T and P.V run on MXFP4
-// operands; the softmax loop applies Pre-Normalization Quantization (PNQ),
+// operands; the online softmax applies Pre-Normalization Quantization (PNQ),
 // i.e. the unnormalized exponentials exp(s - m) are quantized to MXFP4 before
 // they are summed, so the row sum and P.V see the same values.
 //
@@ -104,6 +104,13 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 // no swizzle): offsets at or past the record count read as zero.
 constexpr int kBufferFlags = 0x00020000;
 
+__device__ __forceinline__ const uint8_t* wave_uniform(const uint8_t* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+  return reinterpret_cast<const uint8_t*>((uint64_t(hi) << 32) | lo);
+}
+
 struct __align__(16) TileLds {
   uint8_t k[kBC * 64];
   uint8_t v[128 * 64];
@@ -150,7 +157,9 @@ __device__ __forceinline__ void softmax_group(v4f (&S)[8], float& m, float c, ui
     float p[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) p[i] = fast_exp2(fmaf(S[2 * w + i / 4][i % 4], c, -mc));
-    uint32_t x = 0;
+    // the four converts fill all four bytes, so the first one's merge input
+    // can be any live register; reusing p[0] saves a v_mov per dword
+    uint32_t x = __float_as_uint(p[0]);
     x = cvt_fp4x2<0>(x, p[0], p[1], sc);
     x = cvt_fp4x2<1>(x, p[2], p[3], sc);
     x = cvt_fp4x2<2>(x, p[4], p[5], sc);
@@ -172,7 +181,6 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   constexpr int NT = kWaves * 64;
   constexpr int KI = kBC * 4 / 64;  // wave-wide 16-byte fills per K tile
   constexpr int VI = D * 4 / 64;    // wave-wide 16-byte fills per V tile
-  static_assert(kBC + D <= NT, "one scale word per thread");
   static_assert(KI % kWaves == 0 || kWaves % KI == 0, "fills split evenly over the waves");
   static_assert(VI % kWaves == 0 || kWaves % VI == 0, "fills split evenly over the waves");
   constexpr int KU = (KI + kWaves - 1) / kWaves, VU = (VI + kWaves - 1) / kWaves;  // fills per wave
@@ -228,15 +236,15 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   const int s_lane = lane * 8;
 
   const int ntk = (N + kBC - 1) / kBC;
-  const uint8_t* kc_h = a.kc + bh * int64_t(N) * CROW;
-  const uint8_t* ks_h = a.ks + bh * int64_t(N) * DB;
-  const uint8_t* vc_h = a.vc + bh * int64_t(D) * nbn * 16;
-  const uint8_t* vs_h = a.vs + bh * int64_t(D) * nbn;
+  const uint8_t* kc_h = wave_uniform(a.kc + bh * int64_t(N) * CROW);
+  const uint8_t* ks_h = wave_uniform(a.ks + bh * int64_t(N) * DB);
+  const uint8_t* vc_h = wave_uniform(a.vc + bh * int64_t(D) * nbn * 16);
+  const uint8_t* vs_h = wave_uniform(a.vs + bh * int64_t(D) * nbn);
 
   // Tile fetch.  Code chunks go straight from global memory into LDS (lane i
   // of a wave writes the 16 bytes at dst + 16 i), so the swizzle is applied on
   // the source side: LDS slot s of the K tile holds (row s/4, chunk
-  // (s%4) ^ swizzle(row)).  Scale bytes take a register detour (one VGPR).
+  // (s%4) ^ swizzle(row)).  Scale bytes take a register detour.
   // Per-thread fill offsets (bytes from the tile's base in global memory).
   int koff[KU], voff[VU];
 #pragma unroll
@@ -251,32 +259,46 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
     const int row = slot >> 2;
     voff[u] = (row * nbn + ((slot & 3) ^ v_swz(row))) * 16;
   }
-  // Where this thread's scale bytes go in the lane-ordered layout: byte b of
-  // key tid (tid < kBC) to ks[(16 b + r) * 8 + t], byte b of channel tid - kBC
-  // to vs[(16 b + r) * 8 + ct]; vs follows ks, so one offset from ks serves both.
-  int sdst = 0, snb = 0;
-  if (tid < kBC) {
-    sdst = ((((tid >> 5) << 2) | (tid & 3)) * 8) + ((tid & 31) >> 2);
-    snb = DB;
-  } else if (tid < kBC + D) {
-    const int ch = tid - kBC;
-    sdst = 64 * 8 + (ch & 15) * 8 + (ch >> 4);
-    snb = 4;
-  }
+  // Scale staging.  Thread tid < kBC carries the DB scale bytes of key kb + tid
+  // (one load), thread tid < 4 D one V scale byte (channel tid % D, block
+  // tid / D of the tile); both go to the lane-ordered layout: byte b of key
+  // tid to ks[(16 b + r) * 8 + t], byte b of channel 16 ct + r to
+  // vs[(16 b + r) * 8 + ct] (vs follows ks, so one offset from ks serves both).
+  static_assert(4 * D <= NT, "one V scale byte per thread");
+  const int kdst = ((((tid >> 5) << 2) | (tid & 3)) * 8) + ((tid & 31) >> 2);
+  const int vch = tid % D, vblk = tid / D;
+  const int vdst = 64 * 8 + (vch & 15) * 8 + (vch >> 4) + 128 * vblk;
+  // Threads with no byte to carry load from an offset past every record
+  // count: the range check returns zero without touching memory, and every
+  // thread runs the same instructions.
+  const uint32_t kso = tid < kBC ? uint32_t(tid * DB) : 0x7FFFFFF0u;
+  const uint32_t vso = tid < 4 * D ? uint32_t(vch * nbn + vblk) : 0x7FFFFFF0u;
+  uint32_t kreg = 0, vreg = 0;
 
-  uint32_t sreg = 0;
-  // Code fills use raw buffer loads into LDS: the descriptor's base is the
-  // tile's first byte and its record count the bytes left in the head, so the
-  // hardware range check returns zeros for K rows past N.  V blocks past the
-  // padded end read the next channel's finite data (weight 0) or zeros.
-  const int64_t khead = int64_t(N) * CROW, vhead = int64_t(D) * nbn * 16;
+  // Every fill is a raw buffer load whose descriptor starts at the tile's
+  // first byte and whose record count is the bytes left in the head, so the
+  // hardware range check returns zeros past the end.  K rows past N are zero
+  // (and masked).  V code blocks and V scale bytes past the padded end of a
+  // channel read the next channel's finite data, which meets only zero
+  // weights.
+  const int khead = __builtin_amdgcn_readfirstlane(N * CROW), vhead = __builtin_amdgcn_readfirstlane(D * nbn * 16);
+  const int kshead = __builtin_amdgcn_readfirstlane(N * DB), vshead = __builtin_amdgcn_readfirstlane(D * nbn);
   auto issue_tile = [&](int j, TileLds& T) {
     const int kb = j * kBC;
     const int vb0 = kb / 32;
+    // scales first: the wait for them (at the end of the tile) then does not
+    // cover the code fills issued after them
+    const __amdgpu_buffer_rsrc_t ksrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(ks_h + int64_t(kb) * DB), 0, kshead - kb * DB, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t vsrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(vs_h + vb0), 0, vshead - vb0, kBufferFlags);
+    if constexpr (DB == 4) kreg = __builtin_amdgcn_raw_buffer_load_b32(ksrs, kso, 0, 0);
+    else kreg = __builtin_amdgcn_raw_buffer_load_b16(ksrs, kso, 0, 0);
+    vreg = __builtin_amdgcn_raw_buffer_load_b8(vsrs, vso, 0, 0);
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(kc_h + int64_t(kb) * CROW), 0, int(khead - int64_t(kb) * CROW), kBufferFlags);
+        (void*)(kc_h + int64_t(kb) * CROW), 0, khead - kb * CROW, kBufferFlags);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(vc_h + int64_t(vb0) * 16), 0, int(vhead - int64_t(vb0) * 16), kBufferFlags);
+        (void*)(vc_h + int64_t(vb0) * 16), 0, vhead - vb0 * 16, kBufferFlags);
 #pragma unroll
     for (int u = 0; u < KU; ++u)
       if (KI % kWaves == 0 || wave + u * kWaves < KI)
@@ -287,27 +309,16 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
       if (VI % kWaves == 0 || wave + u * kWaves < VI)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr)(T.v + (wave + u * kWaves) * 1024), 16,
                                                  uint32_t(voff[u]), 0, 0, 0);
-    sreg = 0;
-    if (tid < kBC) {
-      const uint8_t* p = ks_h + int64_t(min(kb + tid, N - 1)) * DB;
-      if (DB == 4) {
-        sreg = *reinterpret_cast<const uint32_t*>(p);
-      } else {
-#pragma unroll
-        for (int b = 0; b < DB; ++b) sreg |= uint32_t(p[b]) << (8 * b);
-      }
-    } else if (tid < kBC + D) {
-      const uint8_t* p = vs_h + int64_t(tid - kBC) * nbn;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) sreg |= uint32_t(p[min(vb0 + b, nbn - 1)]) << (8 * b);
-    }
   };
   auto finish_tile = [&](TileLds& T) {
+    if (tid < kBC) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
-      if (b < snb) T.ks[sdst + 128 * b] = uint8_t(sreg >> (8 * b));
+      for (int b = 0; b < DB; ++b) T.ks[kdst + 128 * b] = uint8_t(kreg >> (8 * b));
+    }
+    if (4 * D == NT || tid < 4 * D) T.ks[vdst] = uint8_t(vreg);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's LDS fills have landed
   };
+
 
   // ---- one key tile: S^T, softmax step, l and O^T updates for every group ----
   auto compute_tile = [&](auto masked, int j, const TileLds& T) {
@@ -366,6 +377,11 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
     MXATTN_PV_STEP(0) MXATTN_PV_STEP(1) MXATTN_PV_STEP(2) MXATTN_PV_STEP(3)
     MXATTN_PV_STEP(4) MXATTN_PV_STEP(5) MXATTN_PV_STEP(6) MXATTN_PV_STEP(7)
 #undef MXATTN_PV_STEP
+    // An empty asm statement that reads the FP4 operands: without it the
+    // compiler sinks the exponentials and converts below the end-of-tile
+    // barrier, and the wait for the next tile's fills comes mid-tile.
+#pragma unroll
+    for (int g = 0; g < kQG; ++g) asm volatile("" ::"v"(pk[g].x), "v"(pk[g].y), "v"(pk[g].z), "v"(pk[g].w));
   };
 
   // ---- tile loop over two LDS buffers ----
@@ -379,6 +395,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
     if (j + 1 < ntk) issue_tile(j + 1, nxt);
     compute_tile(masked, j, cur);
     if (j + 1 < ntk) {
+      // keep the wait for the fills at the end of the tile, so they have the
+      // whole tile's compute to land
+      __builtin_amdgcn_sched_barrier(0);
       finish_tile(nxt);
       __syncthreads();
     }

@@ -10,12 +10,12 @@
  * Source of the method: "MXAttention: Data-Free Optimal Scaling and
  * Pre-Normalization Quantization for MXFP4 Attention" (arXiv 2607.24377),
  * abstract.  The abstract names the pieces and fixes one constant:
- *   - MXFP4 elements share a power-of-two block scale ("microscaling");
+ *   - MXFP4 elements share a power-of-two scale per block;
  *   - OCP MXFP4 is the baseline quantizer;
  *   - Universal Optimal Scaling (UOS) picks the block scale from a fixed,
  *     data-free boundary Qmax = 7.25;
  *   - Pre-Normalization Quantization (PNQ) quantizes the unnormalized
- *     exponentials of the softmax loop before the row sum, so the row sum and
+ *     exponentials of the online softmax before the row sum, so the row sum and
  *     the P.V product see the same quantized values.
  * Everything the abstract leaves open (block size 32, E2M1 elements, E8M0
  * scales, round-to-nearest-even, blocking axes, the running-max schedule,
