@@ -11,6 +11,11 @@ B=1, H=40, N=32760 (21 x 1560 tokens), d=128, UOS + PNQ, non-causal.
 Prints ONE JSON line on stdout; progress goes to stderr.
 
     python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--workload wan]
+
+`--workload sweep` instead times the quantizer alone (mxq_quantize) over
+n = 2^p bf16 values, p = 20..30 (log-uniform magnitudes 2^-20..2^10, random
+sign, viewed [n/1024, 1024]), UOS and OCP along the contiguous axis, plus one
+run along rows at 2^28; the JSON line's value is the 2^30 UOS figure.
 """
 from __future__ import annotations
 
@@ -127,7 +132,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="wan", choices=["tiny", "small", "wan", "hunyuan"])
+    ap.add_argument("--workload", default="wan", choices=["tiny", "small", "wan", "hunyuan", "sweep"])
     ap.add_argument("--mode", default="uos", choices=["uos", "ocp"])
     ap.add_argument("--no-pnq", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -151,6 +156,9 @@ def main():
         log("no GPU visible")
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.workload == "sweep":
+        quantize_sweep(args, dev)
+        return
     cfg = workloads.CONFIGS[args.workload]
     B, H, N, d = cfg["B"], cfg["H"], cfg["N"], cfg["d"]
     BH = B * H
@@ -284,6 +292,95 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(q, k, v, args.workload, mode, pnq, mx.kv_tile(d), gpu_out)
+    print(json.dumps(result), flush=True)
+
+
+def quantize_sweep(args, dev):
+    """The quantizer alone over the sweep sizes (see the module docstring).
+    Each size: `warmup` untimed launches, then `steps` launches, each after a
+    512 MiB fill that evicts the input from the caches and bracketed by HIP
+    events on the launch stream; the median is reported."""
+    import numpy as np
+    import torch
+    import workloads
+    import mxfp4_quantized_attention_amd as mx
+
+    L = mx.lib()
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    flush = torch.empty(512 << 18, dtype=torch.float32, device=dev)
+    cases = [(p, m, 1) for p in (20, 22, 24, 26, 28, 30) for m in ("uos", "ocp")] + [(28, "uos", 0)]
+    rows_out, head = [], None
+    xs = {}
+    for p, mname, axis in cases:
+        n = 1 << p
+        if p not in xs:
+            xs.clear()
+            log(f"[bench] sweep: generating 2^{p}")
+            xs[p] = torch.from_numpy(workloads.sweep(p).view(np.int16)).to(dev)
+        x = xs[p]
+        R, C = n >> 10, 1024
+        nb = (C if axis == 1 else R) // 32
+        nv = R if axis == 1 else C
+        codes = torch.empty(nv * nb * 16, dtype=torch.uint8, device=dev)
+        scales = torch.empty(nv * nb, dtype=torch.uint8, device=dev)
+        mode = mx.MODE_UOS if mname == "uos" else mx.MODE_OCP
+
+        def launch():
+            st = L.mxq_quantize(x.data_ptr(), 1, R, C, axis, mode, codes.data_ptr(), scales.data_ptr(), sp)
+            if st != 0:
+                raise RuntimeError(mx.status_string(st))
+
+        for _ in range(args.warmup):
+            launch()
+        ts = []
+        for _ in range(args.steps):
+            flush.fill_(1.0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            launch()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        us = float(np.median(ts)) * 1e3
+        gbs = 2.53125 * n / (us * 1e-6) / 1e9
+        row = {"p": p, "n": n, "mode": mname, "axis": axis, "us": us, "gbs": gbs,
+               "pct_of_hbm_peak": 100.0 * gbs / PEAK_HBM_GBS}
+        rows_out.append(row)
+        log(f"[bench] sweep 2^{p} {mname} axis {axis}: {us:.1f} us, {gbs:.0f} GB/s")
+        if p == 30 and mname == "uos" and axis == 1:
+            head = row
+            host_codes = codes.cpu().numpy()
+            host_scales = scales.cpu().numpy()
+    result = {
+        "metric": "MXFP4 quantize GB/s (2.53125 B/element: bf16 in, E2M1 codes + E8M0 scales out) "
+                  "and % of MI355X HBM peak",
+        "value": head["gbs"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": head["us"] * 1e-3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16->mxfp4", "data": "synthetic",
+        "config": {"workload": "quantize sweep: n=2^p bf16, p=20..30, viewed [n/1024, 1024], "
+                               "UOS/OCP along the contiguous axis, plus UOS along rows at 2^28; "
+                               "value at 2^30 UOS", "parallelism": "single GPU"},
+        "sweep": rows_out,
+        "roofline": {"bound": "hbm", "achieved": head["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": head["gbs"] / PEAK_HBM_GBS, "traffic": None,
+                     "kernel": "quant_stream_kernel",
+                     "algorithmic": "2 B read + 0.5 B codes + 1/32 B scale per element"},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        log("[bench] cpu baseline (oracle quantizer on the 2^30 input)")
+        xh = workloads.sweep(30)
+        t0 = time.perf_counter()
+        oc, os_ = oracle.quantize_bf16(xh.reshape(1, 1 << 20, 1024), 1, 1 << 20, 1024, 1, oracle.MODE_UOS)
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {
+            "value": 2.53125 * (1 << 30) / dt / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "sample": f"UOS quantization of the 2^30 sweep values (the whole 2^30 case), {dt:.1f} s",
+            "seconds": dt,
+            "bit_exact_vs_gpu_on_sample": bool(np.array_equal(oc.reshape(-1), host_codes)
+                                               and np.array_equal(os_.reshape(-1), host_scales)),
+        }
     print(json.dumps(result), flush=True)
 
 

@@ -17,6 +17,8 @@ namespace mxattn {
 
 namespace {
 
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
@@ -63,7 +65,9 @@ __device__ __forceinline__ uint32_t absmax8_bits(const uint4& v) {
 // Flat stream of full 32-element blocks: block i = elements [32i, 32i + 32)
 // of x, codes [16i, 16i + 16), scale [i].  Four lanes share a block (16 bytes
 // of input each), so a wave reads 1 KiB and writes 256 code bytes per step,
-// both contiguous.  nq = 4 * number of blocks.
+// both contiguous.  nq = 4 * number of blocks.  Input and codes are touched
+// once, so loads and stores carry the non-temporal hint (keeps them from
+// displacing other data in the caches, and measurably faster here).
 template <int MODE, int U>
 __global__ __launch_bounds__(256) void quant_stream_kernel(const uint4* __restrict__ x,
                                                            uint32_t* __restrict__ codes,
@@ -75,7 +79,8 @@ __global__ __launch_bounds__(256) void quant_stream_kernel(const uint4* __restri
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t idx = base + int64_t(u) * 256;
-      v[u] = idx < nq ? x[idx] : make_uint4(0, 0, 0, 0);
+      const v4u t = idx < nq ? __builtin_nontemporal_load(reinterpret_cast<const v4u*>(x) + idx) : v4u{0, 0, 0, 0};
+      v[u] = make_uint4(t.x, t.y, t.z, t.w);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -87,7 +92,7 @@ __global__ __launch_bounds__(256) void quant_stream_kernel(const uint4* __restri
       const int e = block_exp_bf16bits<MODE>(m);
       const uint32_t c = encode8_bf16(v[u], e);
       if (idx < nq) {
-        codes[idx] = c;
+        __builtin_nontemporal_store(c, codes + idx);
         if ((idx & 3) == 0) scales[idx >> 2] = uint8_t(e + 127);
       }
     }
@@ -124,63 +129,93 @@ __global__ __launch_bounds__(256) void quant_rows_general_kernel(const uint16_t*
   scales[b] = uint8_t(e + 127);
 }
 
-// Blocks along rows (axis 0), one column at a time: a 256-row x 64-column
-// bf16 tile is staged in LDS with row-contiguous loads, then each (column,
-// 32-row block) is encoded from LDS and written to the column-major output
-// codes [batch][cols][nb*16].  Rows past the end are zero (padding).
+// Blocks along rows (axis 0).  Work item = a 256-row x 64-column bf16 tile
+// of one batch entry; each workgroup walks items with a grid stride and
+// holds the next item's loads in registers while it encodes the current one
+// from LDS.  Element (row r, column c) of a tile sits at
+// tile[r * 64 + (c ^ 8 (r / 32))], so the eight lanes that read one column
+// of eight 32-row blocks hit eight different banks; eight consecutive lanes
+// take the eight blocks of one column, so a wave writes whole 128-byte code
+// lines.  Rows past the end are zero (padding).
 template <int MODE>
 __global__ __launch_bounds__(256) void quant_cols_kernel(const uint16_t* __restrict__ x,
                                                          uint8_t* __restrict__ codes,
                                                          uint8_t* __restrict__ scales, int64_t rows,
-                                                         int64_t cols, int64_t nb, int64_t ntc) {
+                                                         int64_t cols, int64_t nb, int64_t ntc, int64_t nitems) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[256 * 64];
-  const int64_t bi = blockIdx.y;
-  const int64_t tr = blockIdx.x / ntc, tc = blockIdx.x % ntc;
-  const int64_t r0 = tr * 256, c0 = tc * 64;
-  const uint16_t* xb = x + bi * rows * cols;
   const int tid = threadIdx.x;
-  if ((cols & 7) == 0) {
+  const int ntr = int((rows + 255) / 256);
+  const bool vec8 = (cols & 7) == 0;
+  v4u buf[8];
+  auto load = [&](int64_t item) {
+    const int64_t bi = item / (int64_t(ntr) * ntc), rest = item % (int64_t(ntr) * ntc);
+    const int64_t r0 = (rest / ntc) * 256, c0 = (rest % ntc) * 64;
+    const uint16_t* xb = x + bi * rows * cols;
     const int cc = (tid & 7) * 8;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int rr = (tid >> 3) + 32 * i;
-      uint4 v = make_uint4(0, 0, 0, 0);
+      buf[i] = v4u{0, 0, 0, 0};
       if (r0 + rr < rows && c0 + cc < cols)
-        v = *reinterpret_cast<const uint4*>(xb + (r0 + rr) * cols + c0 + cc);
-      *reinterpret_cast<uint4*>(&tile[rr * 64 + cc]) = v;
+        buf[i] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(xb + (r0 + rr) * cols + c0 + cc));
     }
-  } else {
-    for (int i = tid; i < 256 * 64; i += 256) {
-      const int rr = i >> 6, cc = i & 63;
-      tile[i] = (r0 + rr < rows && c0 + cc < cols) ? xb[(r0 + rr) * cols + c0 + cc] : uint16_t(0);
-    }
-  }
-  __syncthreads();
+  };
+  int64_t item = blockIdx.x;
+  if (vec8 && item < nitems) load(item);
+  for (; item < nitems; item += gridDim.x) {
+    const int64_t bi = item / (int64_t(ntr) * ntc), rest = item % (int64_t(ntr) * ntc);
+    const int64_t tr = rest / ntc, tc = rest % ntc;
+    const int64_t r0 = tr * 256, c0 = tc * 64;
+    if (vec8) {
+      const int cc = (tid & 7) * 8;
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int item = tid + 256 * k;
-    const int c = item & 63, jb = item >> 6;
-    const int64_t blk = tr * 8 + jb;
-    if (c0 + c >= cols || blk >= nb) continue;
-    float f[32];
-    uint32_t m = 0;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const uint32_t h = tile[(32 * jb + i) * 64 + c];
-      m = max(m, h & 0x7FFFu);
-      f[i] = __uint_as_float(h << 16);
+      for (int i = 0; i < 8; ++i) {
+        const int rr = (tid >> 3) + 32 * i;
+        *reinterpret_cast<v4u*>(&tile[rr * 64 + (cc ^ (8 * i))]) = buf[i];
+      }
+    } else {
+      const uint16_t* xb = x + bi * rows * cols;
+      for (int i = tid; i < 256 * 64; i += 256) {
+        const int rr = i >> 6, cc = i & 63;
+        tile[rr * 64 + (cc ^ (8 * (rr >> 5)))] =
+            (r0 + rr < rows && c0 + cc < cols) ? xb[(r0 + rr) * cols + c0 + cc] : uint16_t(0);
+      }
     }
-    const int e = block_exp_bf16bits<MODE>(m);
-    uint4 cw;
-    cw.x = encode8(f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7], e);
-    cw.y = encode8(f[8], f[9], f[10], f[11], f[12], f[13], f[14], f[15], e);
-    cw.z = encode8(f[16], f[17], f[18], f[19], f[20], f[21], f[22], f[23], e);
-    cw.w = encode8(f[24], f[25], f[26], f[27], f[28], f[29], f[30], f[31], e);
-    const int64_t vec = bi * cols + c0 + c;
-    *reinterpret_cast<uint4*>(codes + (vec * nb + blk) * 16) = cw;
-    scales[vec * nb + blk] = uint8_t(e + 127);
+    __syncthreads();
+    if (vec8 && item + gridDim.x < nitems) load(item + gridDim.x);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int it = tid + 256 * k;
+      const int jb = it & 7, c = it >> 3;
+      const int64_t blk = tr * 8 + jb;
+      if (c0 + c >= cols || blk >= nb) continue;
+      float f[32];
+      uint32_t m = 0;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const uint32_t h = tile[(32 * jb + i) * 64 + (c ^ (8 * jb))];
+        m = max(m, h & 0x7FFFu);
+        f[i] = __uint_as_float(h << 16);
+      }
+      const int e = block_exp_bf16bits<MODE>(m);
+      v4u cw;
+      cw.x = encode8(f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7], e);
+      cw.y = encode8(f[8], f[9], f[10], f[11], f[12], f[13], f[14], f[15], e);
+      cw.z = encode8(f[16], f[17], f[18], f[19], f[20], f[21], f[22], f[23], e);
+      cw.w = encode8(f[24], f[25], f[26], f[27], f[28], f[29], f[30], f[31], e);
+      const int64_t vec = bi * cols + c0 + c;
+      __builtin_nontemporal_store(cw, reinterpret_cast<v4u*>(codes + (vec * nb + blk) * 16));
+      scales[vec * nb + blk] = uint8_t(e + 127);
+    }
+    __syncthreads();
   }
 }
+
+// Grid caps: the streaming kernel walks blocks with a grid stride; the column
+// kernel's workgroups each walk tiles (five 32 KiB tiles fit one CU's LDS, so
+// 2560 workgroups are two rounds of 256 CUs x 5).
+constexpr int64_t kStreamGrid = 65536;
+constexpr int64_t kColsGrid = 2560;
 
 // Host-side launchers (stream-ordered, no allocation).  Return the HIP error
 // of the launch.
@@ -191,7 +226,7 @@ hipError_t launch_quantize(const void* x, int64_t batch, int64_t rows, int64_t c
     const int64_t nq = batch * rows * (cols / 32) * 4;
     constexpr int U = 4;
     int64_t grid = (nq + 256 * U - 1) / (256 * U);
-    if (grid > 8192) grid = 8192;
+    if (grid > kStreamGrid) grid = kStreamGrid;
     if (mode == kModeUOS)
       quant_stream_kernel<kModeUOS, U><<<dim3(unsigned(grid)), dim3(256), 0, stream>>>(
           static_cast<const uint4*>(x), reinterpret_cast<uint32_t*>(codes), scales, nq);
@@ -211,13 +246,14 @@ hipError_t launch_quantize(const void* x, int64_t batch, int64_t rows, int64_t c
   } else {
     const int64_t nb = (rows + 31) / 32;
     const int64_t ntr = (rows + 255) / 256, ntc = (cols + 63) / 64;
-    const dim3 grid(unsigned(ntr * ntc), unsigned(batch));
+    const int64_t nitems = batch * ntr * ntc;
+    const int64_t grid = nitems < kColsGrid ? nitems : kColsGrid;
     if (mode == kModeUOS)
-      quant_cols_kernel<kModeUOS><<<grid, dim3(256), 0, stream>>>(static_cast<const uint16_t*>(x),
-                                                                   codes, scales, rows, cols, nb, ntc);
+      quant_cols_kernel<kModeUOS><<<dim3(unsigned(grid)), dim3(256), 0, stream>>>(static_cast<const uint16_t*>(x),
+                                                                   codes, scales, rows, cols, nb, ntc, nitems);
     else
-      quant_cols_kernel<kModeOCP><<<grid, dim3(256), 0, stream>>>(static_cast<const uint16_t*>(x),
-                                                                   codes, scales, rows, cols, nb, ntc);
+      quant_cols_kernel<kModeOCP><<<dim3(unsigned(grid)), dim3(256), 0, stream>>>(static_cast<const uint16_t*>(x),
+                                                                   codes, scales, rows, cols, nb, ntc, nitems);
   }
   return hipGetLastError();
 }
