@@ -2,10 +2,10 @@
 """Benchmark of the MXFP4 attention hot path (MXAttention: UOS + PNQ) on one MI355X.
 
 One step = one pass of the whole path over one batch of synthetic input that
-is already resident in HBM: quantize Q and K along d, quantize V along N, and
-run the fused MXFP4 attention kernel (exactly the launches mxattn_fwd makes,
-issued one by one so each kernel can be bracketed with HIP events on the
-stream it runs on).  Default workload: the Wan-style video DiT shape
+is already resident in HBM: quantize K along d, quantize V along N, and run
+the fused MXFP4 attention kernel, which quantizes Q along d itself (exactly
+the launches mxattn_fwd makes, issued one by one so each kernel can be
+bracketed with HIP events on the stream it runs on).  Default workload: the Wan-style video DiT shape
 B=1, H=40, N=32760 (21 x 1560 tokens), d=128, UOS + PNQ, non-causal.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
@@ -75,17 +75,20 @@ def cpu_baseline(q, k, v, cfg, mode, pnq, kv_tile, gpu_out, heads=8, rows_per_he
     rows = np.concatenate(rows)
     qs, ks, vs = (x.reshape(B * H, N, d)[:heads] for x in (q, k, v))
     t0 = time.perf_counter()
-    ref = oracle.attn_rows(qs, ks, vs, heads, N, d, mode, pnq, kv_tile, 1.0 / np.sqrt(d), rows)
+    ref = oracle.attn_rows(qs, ks, vs, heads, N, d, mode, pnq, kv_tile, 1.0 / np.sqrt(d), rows,
+                           want_budget=False)
     dt = time.perf_counter() - t0
     flop = 4.0 * N * d * rows.size
     got = oracle.bf16_to_f64(gpu_out.reshape(B * H * N, d)[rows])
     want = oracle.bf16_to_f64(ref["out_bf16"])
     diff = np.abs(got - want)
-    # the parity bound of the tests: max(2e-3, one bf16 ulp of the oracle's
-    # value) per element, rows the oracle flags as near a rounding tie exempt
+    # the base parity bound of the tests, max(2e-3, one bf16 ulp of the
+    # oracle's value) per element; rows holding decisions near a rounding tie
+    # may exceed it by the oracle's flip budget, which the timed oracle run
+    # does not compute (the GPU tests check those rows against it)
     ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(want), 1e-30))) - 7)
     ratio = diff / np.maximum(2e-3, ulp)
-    unflagged = ~ref["near_tie"].astype(bool)
+    flagged = ref["near_tie"].astype(bool)
     return {
         "value": flop / dt / 1e12,
         "unit": "TFLOP/s",
@@ -96,8 +99,9 @@ def cpu_baseline(q, k, v, cfg, mode, pnq, kv_tile, gpu_out, heads=8, rows_per_he
         "seconds": dt,
         "vs_gpu_on_sample": {
             "rel_l2": float(np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-300)),
-            "max_diff_over_bound": float(ratio[unflagged].max()) if unflagged.any() else 0.0,
-            "near_tie_rows": int((~unflagged).sum()),
+            "max_diff_over_bound_unflagged_rows": float(ratio[~flagged].max()) if (~flagged).any() else 0.0,
+            "near_tie_rows": int(flagged.sum()),
+            "near_tie_rows_beyond_base_bound": int(np.sum(np.any(ratio[flagged] > 1.0, axis=1))),
         },
     }
 
@@ -176,15 +180,11 @@ def main():
     L = mx.lib()
     nbn = (N + 31) // 32
     u8 = dict(dtype=torch.uint8, device=dev)
-    qc, kc = torch.empty(BH * N * d // 2, **u8), torch.empty(BH * N * d // 2, **u8)
-    qs, ks = torch.empty(BH * N * d // 32, **u8), torch.empty(BH * N * d // 32, **u8)
+    kc, ks = torch.empty(BH * N * d // 2, **u8), torch.empty(BH * N * d // 32, **u8)
     vc, vs = torch.empty(BH * d * nbn * 16, **u8), torch.empty(BH * d * nbn, **u8)
     o = torch.empty_like(qg)
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
-
-    def launch_q():
-        return L.mxq_quantize(qg.data_ptr(), BH, N, d, 1, mode, qc.data_ptr(), qs.data_ptr(), sp)
 
     def launch_k():
         return L.mxq_quantize(kg.data_ptr(), BH, N, d, 1, mode, kc.data_ptr(), ks.data_ptr(), sp)
@@ -193,11 +193,10 @@ def main():
         return L.mxq_quantize(vg.data_ptr(), BH, N, d, 0, mode, vc.data_ptr(), vs.data_ptr(), sp)
 
     def launch_attn():
-        return L.mxattn_fwd_quantized(qc.data_ptr(), qs.data_ptr(), kc.data_ptr(), ks.data_ptr(),
-                                      vc.data_ptr(), vs.data_ptr(), B, H, N, d, mode, pnq, 0.0,
-                                      o.data_ptr(), sp)
+        return L.mxattn_fwd_kv_quantized(qg.data_ptr(), kc.data_ptr(), ks.data_ptr(), vc.data_ptr(),
+                                         vs.data_ptr(), B, H, N, d, mode, pnq, 0.0, o.data_ptr(), sp)
 
-    launches = (launch_q, launch_k, launch_v, launch_attn)
+    launches = (launch_k, launch_v, launch_attn)
 
     def step(ev=None):
         for i, fn in enumerate(launches):
@@ -238,12 +237,12 @@ def main():
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     per_kernel = np.array([[ev[i].elapsed_time(ev[i + 1]) for i in range(len(launches))] for ev in events])
-    kq, kk, kvv, ka = per_kernel.mean(axis=0)
+    kk, kvv, ka = per_kernel.mean(axis=0)
     flop = 4.0 * B * H * N * N * d
     value = flop / (ms_per_step * 1e-3) / 1e12
     achieved = flop / (ka * 1e-3) / 1e12
     log(f"[bench] step {ms_per_step:.3f} ms -> {value:.1f} TFLOP/s; attention kernel {ka:.3f} ms "
-        f"-> {achieved:.1f} TFLOP/s; quantize Q {kq:.3f} K {kk:.3f} V {kvv:.3f} ms")
+        f"-> {achieved:.1f} TFLOP/s; quantize K {kk:.3f} V {kvv:.3f} ms (Q in the attention kernel)")
 
     # the split launches are exactly mxattn_fwd: check bit-equality once
     o_split = o.clone()
@@ -278,7 +277,6 @@ def main():
                      "algorithmic": f"4*d FLOP per score element x B*H*N^2 = {flop:.4g} FLOP per launch"},
         "roofline_quantize": {"bound": "hbm", "unit": "GB/s", "peak": PEAK_HBM_GBS,
                               "bytes_per_launch": qbytes,
-                              "q_axis1_ms": kq, "q_axis1_gbs": qbytes / (kq * 1e-3) / 1e9,
                               "k_axis1_ms": kk, "k_axis1_gbs": qbytes / (kk * 1e-3) / 1e9,
                               "v_axis0_ms": kvv, "v_axis0_gbs": qbytes / (kvv * 1e-3) / 1e9},
         "step_equals_mxattn_fwd": same,

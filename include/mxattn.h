@@ -108,9 +108,10 @@ size_t mxattn_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d);
  *       0 -> it adds the unquantized fp32 exponentials (P.V still uses the
  *            quantized ones; this is the normalization error PNQ removes).
  * softmax_scale: multiplies Q.K^T; <= 0 selects 1/sqrt(d).
- * Steps on `stream`: quantize Q and K along d and V along N into the
- * workspace (mxq_quantize layouts with batch = B*H: Q/K axis 1 with rows = N,
- * cols = d; V axis 0 with rows = N, cols = d), then one fused kernel.  For
+ * Steps on `stream`: quantize K along d and V along N into the workspace
+ * (mxq_quantize layouts with batch = B*H: K axis 1 with rows = N, cols = d;
+ * V axis 0 with rows = N, cols = d), then one fused kernel that quantizes Q
+ * along d itself (same rule and codes as mxq_quantize) and attends.  For
  * every query row and key tile of mxattn_kv_tile(d) keys: S = Q_q K_q^T
  * (fp32), times softmax_scale; running max m; p = exp(s - m) in fp32;
  * p quantized in 32-key blocks aligned to the key index (scale rule = mode);
@@ -136,6 +137,18 @@ int mxattn_fwd(const void *q, const void *k, const void *v, int64_t B, int64_t H
 int mxattn_fwd_quantized(const uint8_t *qc, const uint8_t *qs, const uint8_t *kc, const uint8_t *ks,
                          const uint8_t *vc, const uint8_t *vs, int64_t B, int64_t H, int64_t N,
                          int64_t d, int mode, int pnq, float softmax_scale, void *o, void *stream);
+
+/*
+ * mxattn_fwd_kv_quantized -- the fused kernel of mxattn_fwd alone: bf16 Q as
+ * in mxattn_fwd (quantized inside the kernel), K and V already quantized in
+ * the layouts of mxattn_fwd_quantized (for callers that keep K_q and V_q, and
+ * for timing the kernel by itself).  The result is bit-identical to
+ * mxattn_fwd_quantized on mxq_quantize(Q), and to mxattn_fwd.  Other
+ * arguments and errors as mxattn_fwd (no workspace).
+ */
+int mxattn_fwd_kv_quantized(const void *q, const uint8_t *kc, const uint8_t *ks, const uint8_t *vc,
+                            const uint8_t *vs, int64_t B, int64_t H, int64_t N, int64_t d, int mode,
+                            int pnq, float softmax_scale, void *o, void *stream);
 
 /*
  * mxq_dump -- write quantized data in the reference format "MXQ1": a 256-byte

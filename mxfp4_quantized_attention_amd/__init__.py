@@ -53,6 +53,8 @@ def lib() -> ctypes.CDLL:
     L.mxattn_fwd.restype = i32
     L.mxattn_fwd_quantized.argtypes = [P, P, P, P, P, P, i64, i64, i64, i64, i32, i32, f32, P, P]
     L.mxattn_fwd_quantized.restype = i32
+    L.mxattn_fwd_kv_quantized.argtypes = [P, P, P, P, P, i64, i64, i64, i64, i32, i32, f32, P, P]
+    L.mxattn_fwd_kv_quantized.restype = i32
     L.mxq_dump.argtypes = [ctypes.c_char_p, P, P, i64, i64, i64, i32, i32, P]
     L.mxq_dump.restype = i32
     _lib = L
@@ -60,7 +62,8 @@ def lib() -> ctypes.CDLL:
 
 
 EXPORTS = ("mxq_status_string", "mxattn_version", "mxq_quantize", "mxattn_kv_tile",
-           "mxattn_workspace_bytes", "mxattn_fwd", "mxattn_fwd_quantized", "mxq_dump")
+           "mxattn_workspace_bytes", "mxattn_fwd", "mxattn_fwd_quantized", "mxattn_fwd_kv_quantized",
+           "mxq_dump")
 
 
 def status_string(status: int) -> str:
@@ -158,6 +161,23 @@ def fwd_quantized(qc, qs, kc, ks, vc, vs, B: int, H: int, N: int, d: int, mode="
                                       vc.data_ptr(), vs.data_ptr(), B, H, N, d, _mode(mode),
                                       int(bool(pnq)), float(softmax_scale), o.data_ptr(), _stream(qc)),
            "mxattn_fwd_quantized")
+    return o
+
+
+def fwd_kv_quantized(q, kc, ks, vc, vs, mode="uos", pnq: bool = True, softmax_scale: float = 0.0,
+                     out=None):
+    """The fused kernel of ``fwd`` alone: bf16 Q [B, H, N, d] (quantized in the
+    kernel), K and V already quantized by ``quantize`` (K along d with axis 1,
+    V along N with axis 0, batch = B*H)."""
+    import torch
+    if q.dtype != torch.bfloat16 or q.dim() != 4 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous bf16 [B, H, N, d] tensor")
+    B, H, N, d = q.shape
+    o = torch.empty_like(q) if out is None else out
+    _check(lib().mxattn_fwd_kv_quantized(q.data_ptr(), kc.data_ptr(), ks.data_ptr(), vc.data_ptr(),
+                                         vs.data_ptr(), B, H, N, d, _mode(mode), int(bool(pnq)),
+                                         float(softmax_scale), o.data_ptr(), _stream(q)),
+           "mxattn_fwd_kv_quantized")
     return o
 
 

@@ -15,9 +15,9 @@
 namespace mxattn {
 hipError_t launch_quantize(const void* x, int64_t batch, int64_t rows, int64_t cols, int axis,
                            int mode, uint8_t* codes, uint8_t* scales, hipStream_t stream);
-hipError_t launch_attention(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
-                            const uint8_t* vc, const uint8_t* vs, int BH, int N, int d, int mode,
-                            bool pnq, float softmax_scale, uint16_t* o, hipStream_t stream);
+hipError_t launch_attention(const uint16_t* q, const uint8_t* qc, const uint8_t* qs, const uint8_t* kc,
+                            const uint8_t* ks, const uint8_t* vc, const uint8_t* vs, int BH, int N, int d,
+                            int mode, bool pnq, float softmax_scale, uint16_t* o, hipStream_t stream);
 }  // namespace mxattn
 
 namespace {
@@ -31,19 +31,18 @@ bool valid_mode(int mode) { return mode == MXQ_MODE_OCP || mode == MXQ_MODE_UOS;
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct WsLayout {
-  size_t qc, qs, kc, ks, vc, vs, total;
+  size_t kc, ks, vc, vs, total;
 };
 
-// Workspace regions (each 256-byte aligned): Q codes/scales, K codes/scales
-// (axis 1, rows = N, cols = d) and V codes/scales (axis 0).
+// Workspace regions (each 256-byte aligned): K codes/scales (axis 1, rows = N,
+// cols = d) and V codes/scales (axis 0).  Q is quantized inside the attention
+// kernel and needs none.
 WsLayout ws_layout(int64_t BH, int64_t N, int64_t d) {
   WsLayout w;
   const size_t qcb = size_t(BH * N * d / 2), qsb = size_t(BH * N * (d / 32));
   const int64_t nbn = (N + 31) / 32;
   const size_t vcb = size_t(BH * d * nbn * 16), vsb = size_t(BH * d * nbn);
   size_t off = 0;
-  w.qc = off; off = round256(off + qcb);
-  w.qs = off; off = round256(off + qsb);
   w.kc = off; off = round256(off + qcb);
   w.ks = off; off = round256(off + qsb);
   w.vc = off; off = round256(off + vcb);
@@ -117,9 +116,23 @@ int mxattn_fwd_quantized(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc
   if (!qc || !qs || !kc || !ks || !vc || !vs || !o) return MXQ_ERR_INVALID_ARG;
   if (!aligned16(qc) || !aligned16(kc) || !aligned16(vc) || !aligned16(o)) return MXQ_ERR_INVALID_ARG;
   const float scale = softmax_scale > 0.f ? softmax_scale : float(1.0 / std::sqrt(double(d)));
-  return hip_status(mxattn::launch_attention(qc, qs, kc, ks, vc, vs, int(B * H), int(N), int(d), mode,
-                                             pnq != 0, scale, static_cast<uint16_t*>(o),
+  return hip_status(mxattn::launch_attention(nullptr, qc, qs, kc, ks, vc, vs, int(B * H), int(N), int(d),
+                                             mode, pnq != 0, scale, static_cast<uint16_t*>(o),
                                              static_cast<hipStream_t>(stream)));
+}
+
+int mxattn_fwd_kv_quantized(const void* q, const uint8_t* kc, const uint8_t* ks, const uint8_t* vc,
+                            const uint8_t* vs, int64_t B, int64_t H, int64_t N, int64_t d, int mode, int pnq,
+                            float softmax_scale, void* o, void* stream) {
+  int st = check_attn_sizes(B, H, N, d);
+  if (st != MXQ_OK) return st;
+  if (!valid_mode(mode) || (pnq != 0 && pnq != 1) || !std::isfinite(softmax_scale)) return MXQ_ERR_INVALID_ARG;
+  if (!q || !kc || !ks || !vc || !vs || !o) return MXQ_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(kc) || !aligned16(vc) || !aligned16(o)) return MXQ_ERR_INVALID_ARG;
+  const float scale = softmax_scale > 0.f ? softmax_scale : float(1.0 / std::sqrt(double(d)));
+  return hip_status(mxattn::launch_attention(static_cast<const uint16_t*>(q), nullptr, nullptr, kc, ks, vc, vs,
+                                             int(B * H), int(N), int(d), mode, pnq != 0, scale,
+                                             static_cast<uint16_t*>(o), static_cast<hipStream_t>(stream)));
 }
 
 int mxattn_fwd(const void* q, const void* k, const void* v, int64_t B, int64_t H, int64_t N, int64_t d,
@@ -136,14 +149,13 @@ int mxattn_fwd(const void* q, const void* k, const void* v, int64_t B, int64_t H
   if (!aligned16(workspace)) return MXQ_ERR_INVALID_ARG;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = mxattn::launch_quantize(q, BH, N, d, 1, mode, ws + w.qc, ws + w.qs, s);
-  if (e == hipSuccess) e = mxattn::launch_quantize(k, BH, N, d, 1, mode, ws + w.kc, ws + w.ks, s);
+  hipError_t e = mxattn::launch_quantize(k, BH, N, d, 1, mode, ws + w.kc, ws + w.ks, s);
   if (e == hipSuccess) e = mxattn::launch_quantize(v, BH, N, d, 0, mode, ws + w.vc, ws + w.vs, s);
   if (e != hipSuccess) return MXQ_ERR_HIP;
   const float scale = softmax_scale > 0.f ? softmax_scale : float(1.0 / std::sqrt(double(d)));
-  return hip_status(mxattn::launch_attention(ws + w.qc, ws + w.qs, ws + w.kc, ws + w.ks, ws + w.vc, ws + w.vs,
-                                             int(BH), int(N), int(d), mode, pnq != 0, scale,
-                                             static_cast<uint16_t*>(o), s));
+  return hip_status(mxattn::launch_attention(static_cast<const uint16_t*>(q), nullptr, nullptr, ws + w.kc,
+                                             ws + w.ks, ws + w.vc, ws + w.vs, int(BH), int(N), int(d), mode,
+                                             pnq != 0, scale, static_cast<uint16_t*>(o), s));
 }
 
 int mxq_dump(const char* path, const uint8_t* codes, const uint8_t* scales, int64_t batch, int64_t nvec,

@@ -33,7 +33,8 @@
 namespace mxattn {
 
 struct AttnArgs {
-  const uint8_t* qc;
+  const uint16_t* q;   // bf16 Q [BH][N][D] (in-kernel quantization), or null
+  const uint8_t* qc;   // else Q codes and scales, blocks along d
   const uint8_t* qs;
   const uint8_t* kc;
   const uint8_t* ks;
@@ -173,7 +174,7 @@ __device__ __forceinline__ void softmax_group(v4f (&S)[8], float& m, float c, ui
 
 }  // namespace
 
-template <int D, int MODE, bool PNQ>
+template <int D, int MODE, bool PNQ, bool QBF16>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void attn_fwd_kernel(AttnArgs a) {
   constexpr int DB = D / 32;      // 32-blocks along d in a Q/K row
   constexpr int CROW = D / 2;     // code bytes per Q/K row
@@ -200,7 +201,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   const int N = a.N, nbn = a.nbn;
   const float c = a.c;
 
-  // Q^T operand slices: query r16 of group g, d-block g4.
+  // Q^T operand slices: query r16 of group g, d-block g4.  With bf16 Q the
+  // lane quantizes its own 32-element block here (the same rule and encoder
+  // as the stand-alone quantizer, so the codes are identical).
   uint4 qB[kQG];
   int qS[kQG];
 #pragma unroll
@@ -210,8 +213,17 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
     qS[g] = 127;
     if (qi < N && g4 < DB) {
       const int64_t row = bh * N + qi;
-      qB[g] = *reinterpret_cast<const uint4*>(a.qc + row * CROW + 16 * g4);
-      qS[g] = a.qs[row * DB + g4];
+      if constexpr (QBF16) {
+        const uint4* src = reinterpret_cast<const uint4*>(a.q + row * D + 32 * g4);
+        const uint4 x0 = src[0], x1 = src[1], x2 = src[2], x3 = src[3];
+        const uint32_t amax = max(max(absmax8_bits(x0), absmax8_bits(x1)), max(absmax8_bits(x2), absmax8_bits(x3)));
+        const int e = block_exp_bf16bits<MODE>(amax);
+        qB[g] = make_uint4(encode8_bf16(x0, e), encode8_bf16(x1, e), encode8_bf16(x2, e), encode8_bf16(x3, e));
+        qS[g] = e + 127;
+      } else {
+        qB[g] = *reinterpret_cast<const uint4*>(a.qc + row * CROW + 16 * g4);
+        qS[g] = a.qs[row * DB + g4];
+      }
     }
   }
 
@@ -431,11 +443,11 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   }
 }
 
-hipError_t launch_attention(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
-                            const uint8_t* vc, const uint8_t* vs, int BH, int N, int d, int mode,
-                            bool pnq, float softmax_scale, uint16_t* o, hipStream_t stream) {
+hipError_t launch_attention(const uint16_t* q, const uint8_t* qc, const uint8_t* qs, const uint8_t* kc,
+                            const uint8_t* ks, const uint8_t* vc, const uint8_t* vs, int BH, int N, int d,
+                            int mode, bool pnq, float softmax_scale, uint16_t* o, hipStream_t stream) {
   AttnArgs a;
-  a.qc = qc; a.qs = qs; a.kc = kc; a.ks = ks; a.vc = vc; a.vs = vs; a.o = o;
+  a.q = q; a.qc = qc; a.qs = qs; a.kc = kc; a.ks = ks; a.vc = vc; a.vs = vs; a.o = o;
   a.BH = BH;
   a.N = N;
   a.nbn = (N + 31) / 32;
@@ -444,7 +456,11 @@ hipError_t launch_attention(const uint8_t* qc, const uint8_t* qs, const uint8_t*
   a.per_xcd = (total + 7) / 8;
   a.c = softmax_scale * 1.4426950408889634f;
   const dim3 grid(unsigned(a.per_xcd * 8)), block(kWaves * 64);
-#define MXATTN_LAUNCH(D_, M_, P_) attn_fwd_kernel<D_, M_, P_><<<grid, block, 0, stream>>>(a)
+#define MXATTN_LAUNCH(D_, M_, P_)                                          \
+  do {                                                                      \
+    if (q) attn_fwd_kernel<D_, M_, P_, true><<<grid, block, 0, stream>>>(a);  \
+    else attn_fwd_kernel<D_, M_, P_, false><<<grid, block, 0, stream>>>(a);   \
+  } while (0)
   if (d == 128) {
     if (mode == kModeUOS) { if (pnq) MXATTN_LAUNCH(128, kModeUOS, true); else MXATTN_LAUNCH(128, kModeUOS, false); }
     else { if (pnq) MXATTN_LAUNCH(128, kModeOCP, true); else MXATTN_LAUNCH(128, kModeOCP, false); }

@@ -54,6 +54,52 @@ __device__ __forceinline__ uint32_t cvt_fp4x2(uint32_t old, float a, float b, fl
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, scale, SEL);
 }
 
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Eight fp32 values, block exponent e -> eight E2M1 codes (element 2i in
+// nibble 2i).  y = x / 2^e is exact; the convert divides through its scale
+// operand and rounds.  For e <= -125 a subnormal input could round to a
+// non-zero code, so those (rare) blocks are first multiplied by 2^-e in fp32,
+// which makes every non-zero y normal, and converted with scale 1.
+__device__ __forceinline__ uint32_t encode8(float f0, float f1, float f2, float f3, float f4,
+                                            float f5, float f6, float f7, int e) {
+  float scale;
+  if (e >= -124) {
+    scale = pow2f(e);
+  } else {
+    const float up = pow2f(-e);  // -e in [124, 127]
+    f0 *= up; f1 *= up; f2 *= up; f3 *= up; f4 *= up; f5 *= up; f6 *= up; f7 *= up;
+    scale = 1.0f;
+  }
+  uint32_t r = 0;
+  r = cvt_fp4x2<0>(r, f0, f1, scale);
+  r = cvt_fp4x2<1>(r, f2, f3, scale);
+  r = cvt_fp4x2<2>(r, f4, f5, scale);
+  r = cvt_fp4x2<3>(r, f6, f7, scale);
+  return r;
+}
+
+__device__ __forceinline__ uint32_t encode8_bf16(const uint4& v, int e) {
+  return encode8(bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y), bf16lo(v.z), bf16hi(v.z),
+                 bf16lo(v.w), bf16hi(v.w), e);
+}
+
+// Largest |x| bit pattern of the 8 bf16 values in v (non-negative floats
+// order like their bit patterns).
+__device__ __forceinline__ uint32_t absmax8_bits(const uint4& v) {
+  const uint32_t m = 0x7FFF7FFFu;
+  uint32_t a = v.x & m, b = v.y & m, c = v.z & m, d = v.w & m;
+  auto mx = [](uint32_t p, uint32_t q) {
+    uint32_t lo = max(p & 0xFFFFu, q & 0xFFFFu);
+    uint32_t hi = max(p >> 16, q >> 16);
+    return lo | (hi << 16);
+  };
+  uint32_t t = mx(mx(a, b), mx(c, d));
+  return max(t & 0xFFFFu, t >> 16);
+}
+
+
 // One 16x16x128 MFMA on FP4 operands with E8M0 block scales.
 // A (16 rows x 128 K): lane l holds row l%16, K = 32*(l/16) + [0, 32) as 32
 // nibbles in a[0..3] (nibble n of the 128 bits = K offset n).  B (128 K x 16

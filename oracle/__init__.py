@@ -76,7 +76,7 @@ def _load():
     lib.orc_block_sse_batch.argtypes = [P, i64, i64, i32, i32, P]
     lib.orc_block_sse_batch.restype = None
     lib.orc_attn_rows.argtypes = [P, P, P, i64, i64, i64, i32, i32, i64, ctypes.c_double,
-                                  P, i64, P, P, P, P]
+                                  P, i64, P, P, P, P, P]
     lib.orc_attn_rows.restype = i32
     lib.orc_dump.argtypes = [ctypes.c_char_p, P, P, i64, i64, i64, i32, i32]
     lib.orc_dump.restype = i32
@@ -195,12 +195,14 @@ def block_sse_batch(blocks, e0: int, ne: int) -> np.ndarray:
 
 
 def attn_rows(q, k, v, BH: int, N: int, d: int, mode: int, pnq: bool, Bc: int,
-              softmax_scale: float, rows, want_weights: bool = False):
+              softmax_scale: float, rows, want_weights: bool = False, want_budget: bool = True):
     """Oracle attention for the query rows ``rows`` (flat indices into [BH*N]).
 
     q, k, v: bf16 bit patterns, [BH][N][d].  Returns a dict with
     ``out`` [nrows, d] fp64, ``out_bf16`` [nrows, d] uint16, ``l`` [nrows],
-    ``near_tie`` [nrows] bool and, if asked, ``weights`` [nrows, N].
+    ``near_tie`` [nrows] bool, ``budget`` [nrows, d] (the bound on |dO| when
+    every flagged decision of the row goes the other way; see orc_attn_rows)
+    and, if asked, ``weights`` [nrows, N].
     """
     q = _c(q, np.uint16).reshape(-1)
     k = _c(k, np.uint16).reshape(-1)
@@ -212,14 +214,17 @@ def attn_rows(q, k, v, BH: int, N: int, d: int, mode: int, pnq: bool, Bc: int,
     lsum = np.empty(nr, np.float64)
     flags = np.zeros(nr, np.int32)
     weights = np.empty((nr, N), np.float64) if want_weights else None
+    budget = np.zeros((nr, d), np.float64) if want_budget else None
     rc = _load().orc_attn_rows(_ptr(q), _ptr(k), _ptr(v), BH, N, d, int(mode), int(bool(pnq)),
                                int(Bc), float(softmax_scale), _ptr(rows), nr, _ptr(out),
-                               _ptr(lsum), _ptr(flags), _ptr(weights))
+                               _ptr(lsum), _ptr(flags), _ptr(weights), _ptr(budget))
     if rc != 0:
         raise ValueError("oracle attention rejected its arguments")
     res = {"out": out, "out_bf16": f64_to_bf16(out), "l": lsum, "near_tie": flags != 0}
     if want_weights:
         res["weights"] = weights
+    if want_budget:
+        res["budget"] = budget
     return res
 
 

@@ -314,8 +314,22 @@ static double scale_boundary_distance(double amax, int mode)
  * Blocks whose largest exponential is below 2^-60 are never flagged: their
  * weights cannot reach any output at the acceptance tolerance.  An amax of
  * exactly 1 (the block holding the running max) is exact on every side. */
+/* Largest change of the quantized value of p (block exponent e, quantized
+ * value ph) when p moves by a relative eps either way: the encoder is
+ * monotone, so the two ends of the interval bound every outcome. */
+static double alt_change(double p, double eps, int e, double ph)
+{
+    double lo = orc_e2m1_value(orc_e2m1_encode(ldexp(p * (1.0 - eps), -e)), e);
+    double hi = orc_e2m1_value(orc_e2m1_encode(ldexp(p * (1.0 + eps), -e)), e);
+    return fmax(fabs(lo - ph), fabs(hi - ph));
+}
+
+/* dp_hat (may be NULL): for each element, the largest change of its quantized
+ * value that a flagged decision allows, i.e. the other side of every tie
+ * within eps: its own code, and the block exponent the other side of a scale
+ * boundary would take (0 where nothing is that close). */
 static int quant_p_block(const double *p, const double *t, double m, int n, int mode,
-                         double *p_hat)
+                         double *p_hat, double *dp_hat)
 {
     double amax = 0.0, tmax = -INFINITY;
     for (int i = 0; i < n; ++i) {
@@ -327,14 +341,33 @@ static int quant_p_block(const double *p, const double *t, double m, int n, int 
     int e = orc_block_exponent(amax, mode);
     int near = 0;
     const int relevant = amax >= 0x1p-60;
-    if (relevant && amax != 1.0 &&
-        scale_boundary_distance(amax, mode) < 0x1p-22 * (4.0 + fabs(tmax) + fabs(m)))
+    const double eps_b = 0x1p-22 * (4.0 + fabs(tmax) + fabs(m));
+    if (relevant && amax != 1.0 && scale_boundary_distance(amax, mode) < eps_b)
         near = 1;
     for (int i = 0; i < n; ++i) {
         double y = ldexp(p[i], -e);
         p_hat[i] = orc_e2m1_value(orc_e2m1_encode(y), e);
         if (relevant && y > 0.0 && e2m1_tie_distance(y) < 0x1p-22 * (4.0 + fabs(t[i]) + fabs(m)))
             near = 1;
+    }
+    if (dp_hat) {
+        /* block exponents the other side of a nearby scale boundary */
+        int alt[2], nalt = 0;
+        if (amax > 0.0 && amax != 1.0) {
+            int lo = orc_block_exponent(amax * (1.0 - eps_b), mode);
+            int hi = orc_block_exponent(amax * (1.0 + eps_b), mode);
+            if (lo != e)
+                alt[nalt++] = lo;
+            if (hi != e)
+                alt[nalt++] = hi;
+        }
+        for (int i = 0; i < n; ++i) {
+            const double eps = 0x1p-22 * (4.0 + fabs(t[i]) + fabs(m));
+            double dmax = alt_change(p[i], eps, e, p_hat[i]);
+            for (int a = 0; a < nalt; ++a)
+                dmax = fmax(dmax, alt_change(p[i], eps, alt[a], p_hat[i]));
+            dp_hat[i] = dmax;
+        }
     }
     return near;
 }
@@ -350,7 +383,15 @@ static int quant_p_block(const double *p, const double *t, double m, int n, int 
  *   flags[i]       bit 0: a P decision lay within the fp32 resolution of p
  *                  of a tie (see quant_p_block; may be NULL),
  *   weights[i*N+k] explicit weights w_k with O = sum_k w_k * deq(v_k)
- *                  (may be NULL; costs O(N^2 / Bc) per row).
+ *                  (may be NULL; costs O(N^2 / Bc) per row),
+ *   budget[i*d+c]  a bound on how far O may move when every flagged
+ *                  decision of the row goes the other way (may be NULL):
+ *                  with D_k the largest change of the k-th quantized
+ *                  exponential (quant_p_block), carried through the same
+ *                  rescales as O and l, |dO_c| <= (sum_k D_k |v_kc| +
+ *                  |O_c| sum_k D_k) / (l - sum_k D_k), the l terms only
+ *                  under PNQ (without it l does not use the codes).  Zero
+ *                  for rows with no flagged decision.
  *
  * Readings of the abstract (its only description of the loop is "softmax
  * loop" plus the PNQ sentence):
@@ -370,7 +411,7 @@ static int quant_p_block(const double *p, const double *t, double m, int n, int 
  */
 int orc_attn_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v, int64_t BH, int64_t N,
                   int64_t d, int mode, int pnq, int64_t Bc, double softmax_scale, const int64_t *rows,
-                  int64_t nrows, double *out, double *lsum, int *flags, double *weights)
+                  int64_t nrows, double *out, double *lsum, int *flags, double *weights, double *budget)
 {
     if (BH < 1 || N < 1 || d < 1 || d % 32 != 0 || Bc < 32 || Bc % 32 != 0 || nrows < 0 ||
         (mode != ORC_MODE_OCP && mode != ORC_MODE_UOS && mode != ORC_MODE_NONE))
@@ -441,6 +482,9 @@ int orc_attn_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v, int64
             double *p = (double *)malloc((size_t)N * sizeof(double));
             double *ph = (double *)malloc((size_t)N * sizeof(double));
             double *O = (double *)calloc((size_t)d, sizeof(double));
+            double *dph = budget ? (double *)malloc((size_t)N * sizeof(double)) : NULL;
+            double *Bv = budget ? (double *)calloc((size_t)d, sizeof(double)) : NULL;
+            double Dl = 0.0;
             uint8_t qc[16 * 8], qs[8];
             double *w = weights ? weights + ri * N : NULL;
             int near = 0;
@@ -477,12 +521,27 @@ int orc_attn_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v, int64
                 for (int64_t j = t0; j < t1; ++j)
                     p[j] = (double)(float)exp(t[j] - mnew);
                 if (mode == ORC_MODE_NONE) {
-                    for (int64_t j = t0; j < t1; ++j)
+                    for (int64_t j = t0; j < t1; ++j) {
                         ph[j] = p[j];
+                        if (dph)
+                            dph[j] = 0.0;
+                    }
                 } else {
                     for (int64_t b0 = t0; b0 < t1; b0 += 32) {
                         int n = (int)(t1 - b0 < 32 ? t1 - b0 : 32);
-                        near |= quant_p_block(p + b0, t + b0, mnew, n, mode, ph + b0);
+                        near |= quant_p_block(p + b0, t + b0, mnew, n, mode, ph + b0, dph ? dph + b0 : NULL);
+                    }
+                }
+                if (dph) {
+                    double ds = 0.0;
+                    for (int64_t j = t0; j < t1; ++j)
+                        ds += dph[j];
+                    Dl = alpha * Dl + (pnq ? ds : 0.0);
+                    for (int64_t c = 0; c < d; ++c) {
+                        double acc = 0.0;
+                        for (int64_t j = t0; j < t1; ++j)
+                            acc += dph[j] * fabs(vd[j * d + c]);
+                        Bv[c] = alpha * Bv[c] + acc;
                     }
                 }
                 double rs = 0.0;
@@ -505,6 +564,10 @@ int orc_attn_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v, int64
             }
             for (int64_t c = 0; c < d; ++c)
                 out[ri * d + c] = O[c] / l;
+            if (budget)
+                for (int64_t c = 0; c < d; ++c)
+                    budget[ri * d + c] = (Bv[c] == 0.0 && Dl == 0.0) ? 0.0
+                                         : (l > Dl ? (Bv[c] + fabs(O[c] / l) * Dl) / (l - Dl) : INFINITY);
             if (w)
                 for (int64_t j = 0; j < N; ++j)
                     w[j] /= l;
@@ -512,7 +575,7 @@ int orc_attn_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v, int64
                 lsum[ri] = l;
             if (flags)
                 flags[ri] = near;
-            free(qd); free(t); free(p); free(ph); free(O);
+            free(qd); free(t); free(p); free(ph); free(O); free(dph); free(Bv);
         }
     }
     free(kd); free(vd); free(tmp); free(codes); free(scl);

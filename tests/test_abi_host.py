@@ -45,8 +45,9 @@ def test_workspace_bytes():
     d, N, BH = 128, 32760, 40
     w = mx.workspace_bytes(1, BH, N, d)
     nbn = (N + 31) // 32
-    assert w >= 2 * (BH * N * d // 2 + BH * N * 4) + BH * d * nbn * 17
-    assert w < 2 * (BH * N * d // 2 + BH * N * 4) + BH * d * nbn * 17 + 6 * 256
+    # K codes and scales plus V codes and scales (Q is quantized in the kernel)
+    assert w >= (BH * N * d // 2 + BH * N * 4) + BH * d * nbn * 17
+    assert w < (BH * N * d // 2 + BH * N * 4) + BH * d * nbn * 17 + 4 * 256
     assert mx.workspace_bytes(1, 1, 0, 128) == 0 and mx.workspace_bytes(1, 1, 10, 96) == 0
 
 
@@ -89,6 +90,14 @@ def test_attention_argument_errors():
     assert fwd(H=1 << 21) == UNSUPPORTED
     assert L.mxattn_fwd_quantized(A, A, A, A, A, A, 1, 1, 64, 128, 1, 1, 0.0, None, None) == INVALID
     assert L.mxattn_fwd_quantized(A, A, A, A, A, A, 1, 1, 64, 100, 1, 1, 0.0, A, None) == UNSUPPORTED
+    kvq = L.mxattn_fwd_kv_quantized
+    assert kvq(A, A, A, A, A, 1, 1, 64, 128, 1, 1, 0.0, None, None) == INVALID
+    assert kvq(None, A, A, A, A, 1, 1, 64, 128, 1, 1, 0.0, A, None) == INVALID
+    assert kvq(A + 2, A, A, A, A, 1, 1, 64, 128, 1, 1, 0.0, A, None) == INVALID
+    assert kvq(A, A, A, A, A, 1, 1, 64, 100, 1, 1, 0.0, A, None) == UNSUPPORTED
+    assert kvq(A, A, A, A, A, 1, 1, 0, 128, 1, 1, 0.0, A, None) == INVALID
+    assert kvq(A, A, A, A, A, 1, 1, 64, 128, 3, 1, 0.0, A, None) == INVALID
+    assert kvq(A, A, A, A, A, 1, 1, 64, 128, 1, 1, float("inf"), A, None) == INVALID
 
 
 def test_dump_from_host_memory(tmp_path):

@@ -10,7 +10,10 @@ check it against forms that do not share its structure:
     the row sum) makes V = 1 map to O = 1 exactly and the explicit weights
     sum to one; without PNQ neither holds;
   - Q = 0 makes every exponential 1, so O is the plain mean of the
-    quantized V over the valid keys and l = N (padding never enters).
+    quantized V over the valid keys and l = N (padding never enters);
+  - the flip budget (how far O may move when the decisions flagged as too
+    close to a tie go the other way) bounds the change that nudging the
+    softmax scale by a few fp32 ulps actually causes.
 """
 import numpy as np
 import pytest
@@ -202,3 +205,37 @@ def test_bad_arguments_rejected():
     inf[0, 0] = 0x7F80
     with pytest.raises(ValueError):
         oracle.attn_rows(qb, inf, vb, 1, 64, 64, oracle.MODE_UOS, True, 64, 0.125, [0])
+
+
+@pytest.mark.parametrize("mode,pnq", ALL)
+def test_tie_case_is_flagged_with_a_budget(mode, pnq):
+    qb, kb, vb, scale = workloads.tie_case()
+    r = _run(qb, kb, vb, 256, 64, mode, pnq, 128, scale)
+    assert r["near_tie"].all()
+    assert np.all(r["budget"] > 0)
+
+
+@pytest.mark.parametrize("mode,pnq", ALL)
+def test_flip_budget_covers_perturbed_decisions(mode, pnq):
+    """Nudging the softmax scale by 2^-22 or 1.5 * 2^-23 (relative) moves every
+    t - m by less than the margin within which a decision counts as flagged.
+    On the tie case that pushes the exponentials off their ties and flips
+    codes; on random heads it rarely does.  Each row's change must stay
+    within the unperturbed run's budget plus a small allowance for the
+    smooth part (alpha and, without PNQ, l are not quantized), and flips
+    must occur, or the test would check nothing."""
+    cases = [workloads.tie_case() + (256, 64)]
+    for seed in range(2):
+        qb, kb, vb = _rand_head(100 + seed, 512, 64, scale=2.0)
+        cases.append((qb, kb, vb, 0.125, 512, 64))
+    flipped_rows = 0
+    for qb, kb, vb, scale, N, d in cases:
+        base = _run(qb, kb, vb, N, d, mode, pnq, 128, scale)
+        assert np.all(base["budget"] >= 0)
+        smooth = 1e-4 * np.abs(oracle.bf16_to_f64(vb)).max()
+        for f in (1 + 2.0 ** -22, 1 - 2.0 ** -22, 1 + 1.5 * 2.0 ** -23, 1 - 1.5 * 2.0 ** -23):
+            pert = _run(qb, kb, vb, N, d, mode, pnq, 128, scale * f)
+            diff = np.abs(pert["out"] - base["out"])
+            assert np.all(diff <= base["budget"] + smooth), (N, f, float((diff - base["budget"]).max()))
+            flipped_rows += int(np.sum(diff.max(axis=1) > smooth))
+    assert flipped_rows > 0

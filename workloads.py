@@ -19,6 +19,8 @@ weights, prompts or videos from those models are used or needed):
                                       token indices, shared by Q, K, V and all
                                       heads, scaled x10
   sweep    2^p elements, x = s * 2^U, U ~ Uniform(-20, 10), s = +-1
+  tie_case structured Q/K (and a chosen softmax scale) that put one
+           exponential in eight on an E2M1 rounding tie; V ~ N(0, 1)
 
 Every head of every tensor has its own seed stream, so a single head can be
 regenerated without drawing the rest (the oracle checks sampled rows of the
@@ -140,3 +142,23 @@ def sample_rows(BH: int, N: int, count: int = 512, seed: int = 7) -> np.ndarray:
     rows = set(g.choice(BH * N, size=count, replace=False).tolist())
     rows |= {0, BH * N - 1}
     return np.array(sorted(rows), dtype=np.int64)
+
+
+def tie_case(N: int = 256, d: int = 64, seed: int = 9):
+    """Inputs with one exponential in eight on an E2M1 tie.  Every query is
+    the unit vector e_0; key j has 1.0 in channel 0 when j % 64 == 0, 0.5
+    when j % 8 == 4, and 0 otherwise, so s is 1, 0.5 or 0 (exact in MXFP4).
+    With softmax scale -2 ln(0.3125), the keys with s = 0.5 get
+    p = exp(-0.5 * scale) = 0.3125 up to the fp32 roundings: in a block that
+    holds a maximal key (amax 1, e = -2) that is y = 1.25, the tie between 1
+    and 1.5; in a block without one (amax 0.3125, e = -4) it is y = 5, the tie
+    between 4 and 6.  The keys with s = 0 get p = 0.3125^2, y = 0.39 or 1.56,
+    well away from any tie."""
+    q = np.zeros((N, d), np.float32)
+    q[:, 0] = 1.0
+    k = np.zeros((N, d), np.float32)
+    j = np.arange(N)
+    k[:, 0] = np.where(j % 64 == 0, 1.0, np.where(j % 8 == 4, 0.5, 0.0))
+    v = np.random.default_rng(seed).standard_normal((N, d)).astype(np.float32)
+    scale = float(-2.0 * np.log(0.3125))
+    return f32_to_bf16(q), f32_to_bf16(k), f32_to_bf16(v), scale
