@@ -196,7 +196,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   const int64_t bh = lin / a.ntq;
   const int qt = lin % a.ntq;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // wave index through readfirstlane: the compiler then keeps everything
+  // derived from it (LDS fill destinations) in scalar registers
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g4 = lane >> 4;
   const int N = a.N, nbn = a.nbn;
   const float c = a.c;
@@ -367,11 +369,15 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
 #pragma unroll
     for (int g = 0; g < kQG; ++g) {
       float alpha;
+      // the VALU-heavy part of the tile runs at raised wave priority, so a
+      // SIMD prefers issuing it over waves that sit in their MFMA phases
+      __builtin_amdgcn_s_setprio(1);
       softmax_group<MODE, PNQ>(S[g], m[g], c, pk[g], pS[g], alpha, lpart[g]);
+      __builtin_amdgcn_s_setprio(0);
       if (__any(alpha != 1.0f)) {  // rescale only when some running max moved
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) O[g][ct] *= alpha;
-        if (PNQ) L[g] *= alpha;
+        if (PNQ) L[g][0] *= alpha;  // the four entries are equal; only [0] is read
       }
     }
     if (PNQ) {
