@@ -166,7 +166,12 @@ __device__ __forceinline__ void softmax_group(v4f (&S)[8], float& m, float c, ui
     x = cvt_fp4x2<2>(x, p[4], p[5], sc);
     x = cvt_fp4x2<3>(x, p[6], p[7], sc);
     d[w] = x;
-    if (!PNQ) ps += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    if (!PNQ) {
+      ps += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      // finish this dword's sum before the next dword's exponentials start:
+      // left alone, the compiler runs all 32 exponentials first and spills
+      asm volatile("" : "+v"(ps) : "v"(x));
+    }
   }
   pk = make_uint4(d[0], d[1], d[2], d[3]);
   if (!PNQ) lpart = lpart * alpha + ps;
