@@ -12,6 +12,11 @@ Prints ONE JSON line on stdout; progress goes to stderr.
 
     python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--workload wan]
 
+`--workload gemm` times the MXFP4 GEMM of a DiT linear layer instead: a
+Wan-style FFN up-projection, Y = X W^T with X [32760][5120] bf16 and W
+[13824][5120] quantized once beforehand; one step = quantize X along K, then
+the GEMM kernel (mxgemm's launches).
+
 `--workload sweep` instead times the quantizer alone (mxq_quantize) over
 n = 2^p bf16 values, p = 20..30 (log-uniform magnitudes 2^-20..2^10, random
 sign, viewed [n/1024, 1024]), UOS and OCP along the contiguous axis, plus one
@@ -136,7 +141,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="wan", choices=["tiny", "small", "wan", "hunyuan", "sweep"])
+    ap.add_argument("--workload", default="wan", choices=["tiny", "small", "wan", "hunyuan", "sweep", "gemm"])
     ap.add_argument("--mode", default="uos", choices=["uos", "ocp"])
     ap.add_argument("--no-pnq", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -162,6 +167,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.workload == "sweep":
         quantize_sweep(args, dev)
+        return
+    if args.workload == "gemm":
+        gemm_bench(args, dev)
         return
     cfg = workloads.CONFIGS[args.workload]
     B, H, N, d = cfg["B"], cfg["H"], cfg["N"], cfg["d"]
@@ -290,6 +298,107 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(q, k, v, args.workload, mode, pnq, mx.kv_tile(d), gpu_out)
+    print(json.dumps(result), flush=True)
+
+
+def gemm_bench(args, dev):
+    """The MXFP4 GEMM of a DiT linear layer (see the module docstring)."""
+    import numpy as np
+    import torch
+    import workloads
+    import mxfp4_quantized_attention_amd as mx
+
+    cfg = workloads.GEMM_CONFIGS["gemm"]
+    M, N, K = cfg["M"], cfg["N"], cfg["K"]
+    mode = mx.MODE_UOS if args.mode == "uos" else mx.MODE_OCP
+    log(f"[bench] gemm: generating X [{M}][{K}], W [{N}][{K}]")
+    x, w = workloads.gemm_inputs("gemm")
+    up = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    xg, wg = up(x), up(w)
+    L = mx.lib()
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    u8 = dict(dtype=torch.uint8, device=dev)
+    wc, ws = torch.empty(N * K // 2, **u8), torch.empty(N * K // 32, **u8)
+    if L.mxq_quantize(wg.data_ptr(), 1, N, K, 1, mode, wc.data_ptr(), ws.data_ptr(), sp) != 0:
+        raise RuntimeError("weight quantization failed")
+    xc, xs = torch.empty(M * K // 2, **u8), torch.empty(M * K // 32, **u8)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+    def launch_x():
+        return L.mxq_quantize(xg.data_ptr(), 1, M, K, 1, mode, xc.data_ptr(), xs.data_ptr(), sp)
+
+    def launch_gemm():
+        return L.mxgemm_quantized(xc.data_ptr(), xs.data_ptr(), wc.data_ptr(), ws.data_ptr(), M, N, K,
+                                  y.data_ptr(), sp)
+
+    launches = (launch_x, launch_gemm)
+
+    def step(ev=None):
+        for i, fn in enumerate(launches):
+            if ev is not None:
+                ev[i].record(stream)
+            st = fn()
+            if st != 0:
+                raise RuntimeError(f"launch {i} failed: {mx.status_string(st)}")
+        if ev is not None:
+            ev[len(launches)].record(stream)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(launches) + 1)] for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    per_kernel = np.array([[ev[i].elapsed_time(ev[i + 1]) for i in range(len(launches))] for ev in events])
+    kx, kg = per_kernel.mean(axis=0)
+    flop = 2.0 * M * N * K
+    value = flop / (ms_per_step * 1e-3) / 1e12
+    achieved = flop / (kg * 1e-3) / 1e12
+    log(f"[bench] gemm step {ms_per_step:.3f} ms -> {value:.1f} TFLOP/s; gemm kernel {kg:.3f} ms -> "
+        f"{achieved:.1f} TFLOP/s; quantize X {kx:.3f} ms")
+    y_fwd = mx.gemm(xg, wc, ws, N, mode=args.mode)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(y.view(torch.int16), y_fwd.view(torch.int16)))
+    result = {
+        "metric": "MXFP4 GEMM TFLOP/s (2*M*N*K) of a DiT linear layer, and % of MI355X MXFP4 MFMA peak",
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "mxfp4", "data": "synthetic",
+        "config": {"workload": f"gemm: Y = X W^T, X [{M}][{K}] bf16 quantized per step, W [{N}][{K}] "
+                               f"quantized once, {args.mode.upper()}", "M": M, "N": N, "K": K,
+                   "mode": args.mode, "parallelism": "single GPU"},
+        "pct_of_fp4_peak": 100.0 * value / PEAK_FP4_TFLOPS,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_FP4_TFLOPS, "traffic": None, "kernel": "gemm_kernel",
+                     "kernel_ms": kg, "algorithmic": f"2*M*N*K = {flop:.4g} FLOP per launch"},
+        "quantize_x_ms": kx,
+        "step_equals_mxgemm": same,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        rows = np.sort(np.random.default_rng(13).choice(M, 2048, replace=False))
+        log("[bench] cpu baseline (oracle GEMM on 2048 rows)")
+        t0 = time.perf_counter()
+        ref = oracle.gemm_rows(x, w, M, N, K, mode, rows)
+        dt = time.perf_counter() - t0
+        got = oracle.bf16_to_f64(y.view(torch.int16).cpu().numpy().view(np.uint16)[rows])
+        g = (K / 128 + 16) * 2.0 ** -24
+        err = g * ref["absdot"]
+        ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref["out"]) + err, 1e-30))) - 7)
+        result["cpu_baseline"] = {
+            "value": 2.0 * rows.size * N * K / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": dt,
+            "sample": f"quantization of W and of 2048 seeded X rows, their exact product (numpy fp64), "
+                      f"{dt:.1f} s; FLOP counted as 2*N*K per row",
+            "max_diff_over_bound_on_sample": float((np.abs(got - ref["out"]) / (err + ulp)).max()),
+        }
     print(json.dumps(result), flush=True)
 
 

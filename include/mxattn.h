@@ -151,6 +151,34 @@ int mxattn_fwd_kv_quantized(const void *q, const uint8_t *kc, const uint8_t *ks,
                             int pnq, float softmax_scale, void *o, void *stream);
 
 /*
+ * mxgemm_quantized -- Y = X W^T on MXFP4 operands (the MXAttention abstract's
+ * UOS is data-free, so the same quantizer serves the linear layers around
+ * attention).  X [M][K] and W [N][K] are quantized along K in the canonical
+ * layout of mxq_quantize (batch = 1, axis 1): codes [rows][K/2], scales
+ * [rows][K/32].  Products are exact, sums are fp32 (MFMA), and y receives
+ * bf16 [M][N] rounded to nearest even.  Requires K % 128 == 0 and
+ * N % 4 == 0; code pointers and y 16-byte aligned, scale pointers 4-byte
+ * aligned.  All pointers are device memory owned by the caller.
+ * Errors: MXQ_ERR_INVALID_ARG (null or misaligned pointer, M/N/K < 1),
+ * MXQ_ERR_UNSUPPORTED (K or N not a supported multiple, sizes too large),
+ * MXQ_ERR_HIP.
+ */
+int mxgemm_quantized(const uint8_t *xc, const uint8_t *xs, const uint8_t *wc, const uint8_t *ws,
+                     int64_t M, int64_t N, int64_t K, void *y, void *stream);
+
+/* Bytes of device workspace mxgemm needs for X [M][K] (0 on bad sizes). */
+size_t mxgemm_workspace_bytes(int64_t M, int64_t K);
+
+/*
+ * mxgemm -- the same with bf16 X [M][K]: X is quantized along K with `mode`
+ * into the workspace (mxq_quantize), then multiplied by the pre-quantized W
+ * (weights are quantized once, with mxq_quantize on W [N][K], axis 1).  Other
+ * arguments and errors as mxgemm_quantized, plus MXQ_ERR_WORKSPACE.
+ */
+int mxgemm(const void *x, const uint8_t *wc, const uint8_t *ws, int64_t M, int64_t N, int64_t K,
+           int mode, void *y, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * mxq_dump -- write quantized data in the reference format "MXQ1": a 256-byte
  * header of ASCII JSON padded with spaces and ending in '\n'
  *   {"magic":"MXQ1","version":1,"mode":"ocp"|"uos","axis":A,"batch":B,

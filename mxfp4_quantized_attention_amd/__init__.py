@@ -55,6 +55,12 @@ def lib() -> ctypes.CDLL:
     L.mxattn_fwd_quantized.restype = i32
     L.mxattn_fwd_kv_quantized.argtypes = [P, P, P, P, P, i64, i64, i64, i64, i32, i32, f32, P, P]
     L.mxattn_fwd_kv_quantized.restype = i32
+    L.mxgemm_quantized.argtypes = [P, P, P, P, i64, i64, i64, P, P]
+    L.mxgemm_quantized.restype = i32
+    L.mxgemm_workspace_bytes.argtypes = [i64, i64]
+    L.mxgemm_workspace_bytes.restype = ctypes.c_size_t
+    L.mxgemm.argtypes = [P, P, P, i64, i64, i64, i32, P, P, ctypes.c_size_t, P]
+    L.mxgemm.restype = i32
     L.mxq_dump.argtypes = [ctypes.c_char_p, P, P, i64, i64, i64, i32, i32, P]
     L.mxq_dump.restype = i32
     _lib = L
@@ -63,7 +69,7 @@ def lib() -> ctypes.CDLL:
 
 EXPORTS = ("mxq_status_string", "mxattn_version", "mxq_quantize", "mxattn_kv_tile",
            "mxattn_workspace_bytes", "mxattn_fwd", "mxattn_fwd_quantized", "mxattn_fwd_kv_quantized",
-           "mxq_dump")
+           "mxgemm_quantized", "mxgemm_workspace_bytes", "mxgemm", "mxq_dump")
 
 
 def status_string(status: int) -> str:
@@ -179,6 +185,34 @@ def fwd_kv_quantized(q, kc, ks, vc, vs, mode="uos", pnq: bool = True, softmax_sc
                                          float(softmax_scale), o.data_ptr(), _stream(q)),
            "mxattn_fwd_kv_quantized")
     return o
+
+
+def gemm_quantized(xc, xs, wc, ws, M: int, N: int, K: int, out=None):
+    """Y = X W^T on operands quantized by ``quantize`` (X [M][K] and W [N][K],
+    batch 1, axis 1); returns bf16 [M, N]."""
+    import torch
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=xc.device) if out is None else out
+    _check(lib().mxgemm_quantized(xc.data_ptr(), xs.data_ptr(), wc.data_ptr(), ws.data_ptr(), M, N, K,
+                                  y.data_ptr(), _stream(xc)), "mxgemm_quantized")
+    return y
+
+
+def gemm(x, wc, ws, N: int, mode="uos", out=None, workspace=None):
+    """Y = X W^T with bf16 X [M, K] quantized on the fly and W already
+    quantized (codes, scales of W [N][K], axis 1)."""
+    import torch
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous bf16 [M, K] tensor")
+    M, K = x.shape
+    need = int(lib().mxgemm_workspace_bytes(M, K))
+    if need == 0:
+        raise ValueError(f"unsupported GEMM shape M={M} K={K} (K must be a positive multiple of 128)")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device) if out is None else out
+    _check(lib().mxgemm(x.data_ptr(), wc.data_ptr(), ws.data_ptr(), M, N, K, _mode(mode), y.data_ptr(),
+                        workspace.data_ptr(), workspace.numel(), _stream(x)), "mxgemm")
+    return y
 
 
 def dump(path: str, codes, scales, batch: int, nvec: int, L: int, axis: int, mode="uos") -> None:

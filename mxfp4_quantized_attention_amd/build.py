@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmxattn.so")
-SOURCES = ["abi.hip", "quantize.hip", "attention.hip"]
+SOURCES = ["abi.hip", "quantize.hip", "attention.hip", "gemm.hip"]
 # The attention kernel never sees a NaN (inputs are finite by contract and the
 # running max starts at -inf, never inf - inf); without NaNs the compiler drops
 # the canonicalizing moves it otherwise puts in front of every fmaxf.

@@ -18,6 +18,8 @@ hipError_t launch_quantize(const void* x, int64_t batch, int64_t rows, int64_t c
 hipError_t launch_attention(const uint16_t* q, const uint8_t* qc, const uint8_t* qs, const uint8_t* kc,
                             const uint8_t* ks, const uint8_t* vc, const uint8_t* vs, int BH, int N, int d,
                             int mode, bool pnq, float softmax_scale, uint16_t* o, hipStream_t stream);
+hipError_t launch_gemm(const uint8_t* xc, const uint8_t* xs, const uint8_t* wc, const uint8_t* ws, int M,
+                       int N, int K, uint16_t* y, hipStream_t stream);
 }  // namespace mxattn
 
 namespace {
@@ -63,6 +65,17 @@ int check_attn_sizes(int64_t B, int64_t H, int64_t N, int64_t d) {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MXQ_OK : MXQ_ERR_HIP; }
+
+int check_gemm_sizes(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || N < 1 || K < 1) return MXQ_ERR_INVALID_ARG;
+  if (K % 128 != 0 || N % 4 != 0) return MXQ_ERR_UNSUPPORTED;
+  // codes of X and W, and Y, addressed with 32-bit offsets per tile
+  if (M * (K / 2) > (int64_t(1) << 31) - 1 || N * (K / 2) > (int64_t(1) << 31) - 1) return MXQ_ERR_UNSUPPORTED;
+  if (M > (int64_t(1) << 30) || N > (int64_t(1) << 30) || M * N > (int64_t(1) << 40)) return MXQ_ERR_UNSUPPORTED;
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  if (tiles + 8 > (int64_t(1) << 31) - 1) return MXQ_ERR_UNSUPPORTED;
+  return MXQ_OK;
+}
 
 }  // namespace
 
@@ -156,6 +169,41 @@ int mxattn_fwd(const void* q, const void* k, const void* v, int64_t B, int64_t H
   return hip_status(mxattn::launch_attention(static_cast<const uint16_t*>(q), nullptr, nullptr, ws + w.kc,
                                              ws + w.ks, ws + w.vc, ws + w.vs, int(BH), int(N), int(d), mode,
                                              pnq != 0, scale, static_cast<uint16_t*>(o), s));
+}
+
+size_t mxgemm_workspace_bytes(int64_t M, int64_t K) {
+  if (M < 1 || K < 1 || K % 128 != 0 || M * (K / 2) > (int64_t(1) << 31) - 1) return 0;
+  return round256(size_t(M * K / 2)) + round256(size_t(M * K / 32));
+}
+
+int mxgemm_quantized(const uint8_t* xc, const uint8_t* xs, const uint8_t* wc, const uint8_t* ws, int64_t M,
+                     int64_t N, int64_t K, void* y, void* stream) {
+  int st = check_gemm_sizes(M, N, K);
+  if (st != MXQ_OK) return st;
+  if (!xc || !xs || !wc || !ws || !y) return MXQ_ERR_INVALID_ARG;
+  if (!aligned16(xc) || !aligned16(wc) || !aligned16(y)) return MXQ_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(xs) & 3u) || (reinterpret_cast<uintptr_t>(ws) & 3u)) return MXQ_ERR_INVALID_ARG;
+  return hip_status(mxattn::launch_gemm(xc, xs, wc, ws, int(M), int(N), int(K), static_cast<uint16_t*>(y),
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int mxgemm(const void* x, const uint8_t* wc, const uint8_t* ws, int64_t M, int64_t N, int64_t K, int mode,
+           void* y, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_gemm_sizes(M, N, K);
+  if (st != MXQ_OK) return st;
+  if (!valid_mode(mode)) return MXQ_ERR_INVALID_ARG;
+  if (!x || !wc || !ws || !y) return MXQ_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(wc) || !aligned16(y)) return MXQ_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(ws) & 3u) return MXQ_ERR_INVALID_ARG;
+  const size_t need = mxgemm_workspace_bytes(M, K);
+  if (!workspace || workspace_bytes < need) return MXQ_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return MXQ_ERR_INVALID_ARG;
+  uint8_t* xc = static_cast<uint8_t*>(workspace);
+  uint8_t* xs = xc + round256(size_t(M * K / 2));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = mxattn::launch_quantize(x, 1, M, K, 1, mode, xc, xs, s);
+  if (e != hipSuccess) return MXQ_ERR_HIP;
+  return hip_status(mxattn::launch_gemm(xc, xs, wc, ws, int(M), int(N), int(K), static_cast<uint16_t*>(y), s));
 }
 
 int mxq_dump(const char* path, const uint8_t* codes, const uint8_t* scales, int64_t batch, int64_t nvec,

@@ -1,0 +1,255 @@
+// gemm.hip -- MXFP4 GEMM for gfx950: Y = X W^T.
+//
+// MXAttention (arXiv 2607.24377), abstract: UOS picks MXFP4 block scales from
+// a fixed, data-free boundary (Qmax = 7.25), so the same quantizer serves any
+// MXFP4 contraction, not only attention.  Here X [M][K] (activations) and
+// W [N][K] (weights) are both quantized along K in the canonical layout of
+// mxq_quantize (codes [rows][K/2], scales [rows][K/32]); the products run on
+// the scaled FP4 MFMA with fp32 accumulation and Y is rounded to bf16.
+//
+// Kernel structure: one workgroup computes a 256 x 256 tile of Y with 8 waves
+// (4 along M x 2 along N, 64 x 128 each) at two waves per SIMD.  K advances
+// 256 at a time: the W and X code tiles of the next step stream from global
+// memory straight into the other half of a double-buffered LDS while the
+// current step runs 64 MFMAs per wave, and one barrier per step publishes it.
+// The MFMA computes Y^T tiles (A = 16 rows of W, B = 16 rows of X), so each
+// lane ends up with four consecutive n of one m: one 8-byte store.
+#include <type_traits>
+
+#include "mx_device.h"
+
+namespace mxattn {
+
+struct GemmArgs {
+  const uint8_t* xc;  // X codes [M][K/2], scales [M][K/32]
+  const uint8_t* xs;
+  const uint8_t* wc;  // W codes [N][K/2], scales [N][K/32]
+  const uint8_t* ws;
+  uint16_t* y;        // bf16 [M][N]
+  int M, N, K;
+  int tn;             // tiles along N
+  int ntiles;         // tiles in all
+  int per_xcd;        // workgroups per XCD in the tile order below
+};
+
+constexpr int kGM = 256, kGN = 256;  // workgroup tile
+constexpr int kGK = 256;             // K per step: two 128-deep MFMA chunks
+constexpr int kGWaves = 8;
+
+namespace {
+
+// LDS of one K step.  Codes: row-major, 128 bytes per row (two 64-byte
+// chunks of 128 K, one per MFMA depth), the four 16-byte pieces of each
+// 64-byte chunk XOR-swizzled by the row so that the 16 lanes reading one
+// MFMA operand (rows 16t + r, piece g) hit distinct banks whether the LDS
+// serves 8 lanes from 32 banks or 16 lanes from 64.  Scales: lane order,
+// sl[h][(g * 16 + r) * 16 + t] = scale of row 16t + r, block g of chunk h.
+struct __align__(16) GemmLds {
+  uint8_t w[kGN * 128];
+  uint8_t x[kGM * 128];
+  uint8_t wsl[2][64 * 16];
+  uint8_t xsl[2][64 * 16];
+};
+
+__device__ __forceinline__ int gswz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit format, range checked
+
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+  return reinterpret_cast<const uint8_t*>((uint64_t(hi) << 32) | lo);
+}
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(kGWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void gemm_kernel(GemmArgs a) {
+  constexpr int NT = kGWaves * 64;
+  // two separate objects (not an array): the compiler then knows that the
+  // fills into one buffer cannot alias the operand reads from the other
+  __shared__ GemmLds lds0, lds1;
+
+  // Tile order: workgroup w runs on XCD w % 8; each XCD takes a contiguous
+  // range of tiles, M-major, so the workgroups of one XCD share X rows (and
+  // sweep W) through that XCD's L2.
+  const int w = blockIdx.x;
+  const int lin = (w & 7) * a.per_xcd + (w >> 3);
+  if (lin >= a.ntiles) return;
+  const int m0 = (lin / a.tn) * kGM, n0 = (lin % a.tn) * kGN;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int wm = wave & 3, wn = wave >> 2;  // wave tile: rows 64 wm of X, rows 128 wn of W
+  const int K = a.K, KC = K / 2, KS = K / 32;
+  const int nsteps = (K + kGK - 1) / kGK;
+
+  const uint8_t* xc_t = uniform_ptr(a.xc + int64_t(m0) * KC);
+  const uint8_t* wc_t = uniform_ptr(a.wc + int64_t(n0) * KC);
+  const uint8_t* xs_t = uniform_ptr(a.xs + int64_t(m0) * KS);
+  const uint8_t* ws_t = uniform_ptr(a.ws + int64_t(n0) * KS);
+  const int xc_bytes = __builtin_amdgcn_readfirstlane((a.M - m0) * KC);
+  const int wc_bytes = __builtin_amdgcn_readfirstlane((a.N - n0) * KC);
+  const int xs_bytes = __builtin_amdgcn_readfirstlane((a.M - m0) * KS);
+  const int ws_bytes = __builtin_amdgcn_readfirstlane((a.N - n0) * KS);
+
+  // Code fills: 256 rows x 128 bytes per operand = 2048 16-byte pieces, four
+  // per thread per operand.  Slot s = (wave + 8u) * 64 + lane of the region
+  // holds row s / 8, chunk (s / 4) % 2, piece (s % 4) ^ gswz(row).  Rows past
+  // M or N read as zero through the descriptor's range check.
+  uint32_t foff[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int s = (wave + kGWaves * u) * 64 + lane;
+    const int row = s >> 3, h = (s >> 2) & 1, piece = (s & 3) ^ gswz(row & 15);
+    foff[u] = uint32_t(row * KC + h * 64 + piece * 16);
+  }
+  // Scale staging: thread tid < 256 carries the 8 scale bytes (blocks of the
+  // step) of W row tid, the others those of X row tid - 256.
+  const int srow = tid & 255;
+  const uint32_t soff = uint32_t(srow * KS);
+  const int sdst = ((srow & 15) * 16) + (srow >> 4);  // + (g * 16) * 16 per block g
+  uint32_t sreg0 = 0, sreg1 = 0;
+
+  auto issue = [&](int step, GemmLds& T) {
+    const int kb = step * kGK;
+    const int sb = __builtin_amdgcn_readfirstlane(kb / 32);
+    // waves 0-3 (threads 0-255) stage W scales, waves 4-7 X scales: the
+    // choice is wave-uniform, so the descriptor stays scalar
+    const __amdgpu_buffer_rsrc_t srs = wave < 4
+        ? __builtin_amdgcn_make_buffer_rsrc((void*)(ws_t + sb), 0, ws_bytes - sb, kBufferFlags)
+        : __builtin_amdgcn_make_buffer_rsrc((void*)(xs_t + sb), 0, xs_bytes - sb, kBufferFlags);
+    sreg0 = __builtin_amdgcn_raw_buffer_load_b32(srs, soff, 0, 0);
+    sreg1 = __builtin_amdgcn_raw_buffer_load_b32(srs, soff + 4, 0, 0);
+    const int cb = __builtin_amdgcn_readfirstlane(kb / 2);
+    const __amdgpu_buffer_rsrc_t wrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(wc_t + cb), 0, wc_bytes - cb, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t xrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(xc_t + cb), 0, xc_bytes - cb, kBufferFlags);
+    // (wave & 7): a provably small offset lets the compiler see that these
+    // fills stay inside T and cannot alias reads of the other buffer
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (lds_ptr)(T.w + ((wave & 7) + kGWaves * u) * 1024), 16, foff[u], 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (lds_ptr)(T.x + ((wave & 7) + kGWaves * u) * 1024), 16, foff[u], 0, 0, 0);
+  };
+  auto finish = [&](GemmLds& T) {
+    uint8_t* sl = wave < 4 ? &T.wsl[0][0] : &T.xsl[0][0];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const uint32_t v = b < 4 ? sreg0 : sreg1;
+      sl[(b >> 2) * 1024 + (b & 3) * 256 + sdst] = uint8_t(v >> (8 * (b & 3)));
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's LDS fills have landed
+  };
+
+  v4f acc[8][4];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[j][i] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // per-lane LDS offsets: operand row 16t + r16, piece g4 of chunk h
+  const int w_lane = (128 * wn + r16) * 128 + 16 * (g4 ^ gswz(r16));
+  const int x_lane = (64 * wm + r16) * 128 + 16 * (g4 ^ gswz(r16));
+  const int ws_lane = (g4 * 16 + r16) * 16 + 8 * wn;
+  const int xs_lane = (g4 * 16 + r16) * 16 + 4 * wm;
+
+  auto compute = [&](const GemmLds& T, auto nchunks) {
+    constexpr int NCH = decltype(nchunks)::value;
+#pragma unroll
+    for (int h = 0; h < NCH; ++h) {
+      const uint2 wsc = *reinterpret_cast<const uint2*>(&T.wsl[h][ws_lane]);
+      const uint32_t xsc = *reinterpret_cast<const uint32_t*>(&T.xsl[h][xs_lane]);
+      uint4 xb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xb[i] = *reinterpret_cast<const uint4*>(&T.x[x_lane + i * 16 * 128 + 64 * h]);
+#define MXGEMM_ROW(j_)                                                                             \
+      {                                                                                            \
+        const uint4 wa = *reinterpret_cast<const uint4*>(&T.w[w_lane + (j_) * 16 * 128 + 64 * h]); \
+        const int sa = int((j_) < 4 ? wsc.x : wsc.y);                                             \
+        acc[j_][0] = mfma_fp4_16x16x128<(j_) & 3, 0>(wa, xb[0], acc[j_][0], sa, int(xsc));         \
+        acc[j_][1] = mfma_fp4_16x16x128<(j_) & 3, 1>(wa, xb[1], acc[j_][1], sa, int(xsc));         \
+        acc[j_][2] = mfma_fp4_16x16x128<(j_) & 3, 2>(wa, xb[2], acc[j_][2], sa, int(xsc));         \
+        acc[j_][3] = mfma_fp4_16x16x128<(j_) & 3, 3>(wa, xb[3], acc[j_][3], sa, int(xsc));         \
+      }
+      MXGEMM_ROW(0) MXGEMM_ROW(1) MXGEMM_ROW(2) MXGEMM_ROW(3)
+      MXGEMM_ROW(4) MXGEMM_ROW(5) MXGEMM_ROW(6) MXGEMM_ROW(7)
+#undef MXGEMM_ROW
+    }
+  };
+
+  // K loop over two LDS buffers, unrolled by two so the buffers are constants.
+  // Inside the loop every step has a successor, so its fills are issued with
+  // no branch around them (a conditional fill makes the compiler wait for it
+  // before the next operand reads); the last one or two steps follow.
+  const bool half_last = (K % kGK) != 0;  // K % 256 == 128: the last step has one chunk
+  const std::integral_constant<int, 1> one_chunk;
+  const std::integral_constant<int, 2> two_chunks;
+  auto step = [&](int s, const GemmLds& cur, GemmLds& nxt) {
+    issue(s + 1, nxt);
+    compute(cur, two_chunks);
+    __builtin_amdgcn_sched_barrier(0);
+    finish(nxt);
+    __syncthreads();
+  };
+  issue(0, lds0);
+  finish(lds0);
+  __syncthreads();
+  int s = 0;
+  for (; s + 2 < nsteps; s += 2) {
+    step(s, lds0, lds1);
+    step(s + 1, lds1, lds0);
+  }
+  const GemmLds* last = &lds0;
+  if (s + 1 < nsteps) {
+    step(s, lds0, lds1);
+    last = &lds1;
+  }
+  if (half_last)
+    compute(*last, one_chunk);
+  else
+    compute(*last, two_chunks);
+
+  // epilogue: acc[j][i] is the Y^T tile of W rows 128 wn + 16 j and X rows
+  // 64 wm + 16 i; lane: m = r16 of it, n = 4 g4 + [0, 4)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + 64 * wm + 16 * i + r16;
+    if (m >= a.M) continue;
+    uint16_t* yrow = a.y + int64_t(m) * a.N;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int n = n0 + 128 * wn + 16 * j + 4 * g4;
+      if (n < a.N) {
+        const uint32_t b0 = f32_to_bf16_rne(acc[j][i][0]), b1 = f32_to_bf16_rne(acc[j][i][1]);
+        const uint32_t b2 = f32_to_bf16_rne(acc[j][i][2]), b3 = f32_to_bf16_rne(acc[j][i][3]);
+        *reinterpret_cast<uint2*>(yrow + n) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+      }
+    }
+  }
+}
+
+hipError_t launch_gemm(const uint8_t* xc, const uint8_t* xs, const uint8_t* wc, const uint8_t* ws, int M,
+                       int N, int K, uint16_t* y, hipStream_t stream) {
+  GemmArgs a;
+  a.xc = xc; a.xs = xs; a.wc = wc; a.ws = ws; a.y = y;
+  a.M = M; a.N = N; a.K = K;
+  const int tm = (M + kGM - 1) / kGM;
+  a.tn = (N + kGN - 1) / kGN;
+  a.ntiles = tm * a.tn;
+  a.per_xcd = (a.ntiles + 7) / 8;
+  gemm_kernel<<<dim3(unsigned(a.per_xcd * 8)), dim3(kGWaves * 64), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace mxattn

@@ -228,6 +228,32 @@ def attn_rows(q, k, v, BH: int, N: int, d: int, mode: int, pnq: bool, Bc: int,
     return res
 
 
+def gemm_rows(x, w, M: int, N: int, K: int, mode: int, rows=None):
+    """Oracle MXFP4 GEMM: Y = X_q W_q^T for the rows ``rows`` of X (all rows if
+    None).  x: bf16 bits [M][K], w: bf16 bits [N][K]; both are quantized
+    along K with ``mode`` by this oracle's quantizer (MODE_NONE: used as they
+    are), dequantized, and multiplied in fp64 (a library matmul; the products
+    of dequantized MXFP4 values are exact and fp64 sums of K of them lose
+    nothing the acceptance can see).  Returns ``out`` [nr, N] fp64,
+    ``out_bf16`` (round to nearest even) and ``absdot`` [nr, N] = |X_q| |W_q|^T,
+    the scale of the fp32 accumulation error a GPU may add."""
+    x = _c(x, np.uint16).reshape(M, K)
+    w = _c(w, np.uint16).reshape(N, K)
+    rows = np.arange(M, dtype=np.int64) if rows is None else _c(rows, np.int64).reshape(-1)
+    xr = np.ascontiguousarray(x[rows])
+    if mode == MODE_NONE:
+        xd = bf16_to_f64(xr).reshape(rows.size, K)
+        wd = bf16_to_f64(w).reshape(N, K)
+    else:
+        xcod, xsc = quantize_bf16(xr, 1, rows.size, K, 1, mode)
+        wcod, wsc = quantize_bf16(w, 1, N, K, 1, mode)
+        xd = dequantize(xcod, xsc, rows.size, K)
+        wd = dequantize(wcod, wsc, N, K)
+    out = xd @ wd.T
+    absdot = np.abs(xd) @ np.abs(wd).T
+    return {"out": out, "out_bf16": f64_to_bf16(out), "absdot": absdot}
+
+
 def dump(path: str, codes, scales, batch: int, nvec: int, L: int, axis: int, mode: int) -> None:
     codes = _c(codes, np.uint8)
     scales = _c(scales, np.uint8)

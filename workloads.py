@@ -19,6 +19,9 @@ weights, prompts or videos from those models are used or needed):
                                       token indices, shared by Q, K, V and all
                                       heads, scaled x10
   sweep    2^p elements, x = s * 2^U, U ~ Uniform(-20, 10), s = +-1
+  gemm     X [32760][5120] (Wan-style tokens x hidden: Student-t(4) times a
+           LogNormal(0, 1) scale per channel), W [13824][5120] (an FFN
+           up-projection) ~ N(0, 0.02^2); both bf16
   tie_case structured Q/K (and a chosen softmax scale) that put one
            exponential in eight on an E2M1 rounding tie; V ~ N(0, 1)
 
@@ -162,3 +165,41 @@ def tie_case(N: int = 256, d: int = 64, seed: int = 9):
     v = np.random.default_rng(seed).standard_normal((N, d)).astype(np.float32)
     scale = float(-2.0 * np.log(0.3125))
     return f32_to_bf16(q), f32_to_bf16(k), f32_to_bf16(v), scale
+
+
+GEMM_CONFIGS = {
+    "gemm": dict(M=32760, N=13824, K=5120, seed=5),
+}
+
+
+def gemm_inputs(name: str = "gemm", M: int | None = None, N: int | None = None, K: int | None = None,
+                seed: int | None = None, threads: int | None = None):
+    """X [M][K] and W [N][K] as bf16 bit patterns.  X rows are tokens with a
+    per-channel LogNormal(0, 1) scale on Student-t(4) entries; W ~ N(0, 0.02^2).
+    Rows are drawn in chunks with their own seed streams, so any row range
+    can be regenerated alone."""
+    cfg = GEMM_CONFIGS.get(name, {})
+    M = cfg["M"] if M is None else M
+    N = cfg["N"] if N is None else N
+    K = cfg["K"] if K is None else K
+    seed = cfg.get("seed", 5) if seed is None else seed
+    chan = np.exp(_rng(seed, 20, K).standard_normal(K)).astype(np.float32)
+    x = np.empty((M, K), np.uint16)
+    w = np.empty((N, K), np.uint16)
+    rows = 1024
+
+    def fill_x(ci):
+        g = _rng(seed, 21, M, K, ci)
+        r0, r1 = ci * rows, min(M, (ci + 1) * rows)
+        x[r0:r1] = f32_to_bf16(g.standard_t(4.0, size=(r1 - r0, K)).astype(np.float32) * chan[None, :])
+
+    def fill_w(ci):
+        g = _rng(seed, 22, N, K, ci)
+        r0, r1 = ci * rows, min(N, (ci + 1) * rows)
+        w[r0:r1] = f32_to_bf16(g.standard_normal((r1 - r0, K), dtype=np.float32) * np.float32(0.02))
+
+    nt = threads or min(16, os.cpu_count() or 1)
+    with ThreadPoolExecutor(max_workers=nt) as ex:
+        list(ex.map(fill_x, range((M + rows - 1) // rows)))
+        list(ex.map(fill_w, range((N + rows - 1) // rows)))
+    return x, w
