@@ -39,10 +39,12 @@ constexpr int kGWaves = 8;
 namespace {
 
 // LDS of one K step.  Codes: row-major, 128 bytes per row (two 64-byte
-// chunks of 128 K, one per MFMA depth), the four 16-byte pieces of each
-// 64-byte chunk XOR-swizzled by the row so that the 16 lanes reading one
-// MFMA operand (rows 16t + r, piece g) hit distinct banks whether the LDS
-// serves 8 lanes from 32 banks or 16 lanes from 64.  Scales: lane order,
+// chunks of 128 K, one per MFMA depth); the eight 16-byte pieces of a row
+// are XOR-swizzled by the row (piece p at slot p ^ gswz(row % 16)) so that
+// the 16 lanes reading one MFMA operand (rows 16t + r, one piece) hit
+// distinct banks whether the LDS serves 8 lanes from 32 banks or 16 lanes
+// from 64: gswz is one-to-one on any 8 consecutive rows and on the even and
+// on the odd rows of a 16-row tile.  Scales: lane order,
 // sl[h][(g * 16 + r) * 16 + t] = scale of row 16t + r, block g of chunk h.
 struct __align__(16) GemmLds {
   uint8_t w[kGN * 128];
@@ -51,7 +53,7 @@ struct __align__(16) GemmLds {
   uint8_t xsl[2][64 * 16];
 };
 
-__device__ __forceinline__ int gswz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+__device__ __forceinline__ int gswz(int row) { return (row & 7) ^ (row >> 3); }
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit format, range checked
@@ -77,13 +79,18 @@ __global__ __launch_bounds__(kGWaves * 64) __attribute__((amdgpu_waves_per_eu(2)
   // fills into one buffer cannot alias the operand reads from the other
   __shared__ GemmLds lds0, lds1;
 
-  // Tile order: workgroup w runs on XCD w % 8; each XCD takes a contiguous
-  // range of tiles, M-major, so the workgroups of one XCD share X rows (and
-  // sweep W) through that XCD's L2.
+  // Tile order: workgroup w runs on XCD w % 8 and each XCD takes a
+  // contiguous range of tiles.  Tiles come in groups of 8 M tiles:
+  // consecutive tiles walk the 8 M tiles of a group for one N tile, so the
+  // tiles in flight on an XCD share X rows and W rows through its L2.
   const int w = blockIdx.x;
   const int lin = (w & 7) * a.per_xcd + (w >> 3);
   if (lin >= a.ntiles) return;
-  const int m0 = (lin / a.tn) * kGM, n0 = (lin % a.tn) * kGN;
+  const int tmc = a.ntiles / a.tn;
+  const int gsz = 8 * a.tn;
+  const int gid = lin / gsz, rr = lin % gsz;
+  const int gm = min(8, tmc - 8 * gid);
+  const int m0 = (8 * gid + rr % gm) * kGM, n0 = (rr / gm) * kGN;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g4 = lane >> 4;
@@ -102,14 +109,15 @@ __global__ __launch_bounds__(kGWaves * 64) __attribute__((amdgpu_waves_per_eu(2)
 
   // Code fills: 256 rows x 128 bytes per operand = 2048 16-byte pieces, four
   // per thread per operand.  Slot s = (wave + 8u) * 64 + lane of the region
-  // holds row s / 8, chunk (s / 4) % 2, piece (s % 4) ^ gswz(row).  Rows past
-  // M or N read as zero through the descriptor's range check.
+  // holds row s / 8, piece (s % 8) ^ gswz(row % 16) of that row (pieces
+  // 0-3: the first 128 K of the step, 4-7: the second).  Rows past M or N
+  // read as zero through the descriptor's range check.
   uint32_t foff[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int s = (wave + kGWaves * u) * 64 + lane;
-    const int row = s >> 3, h = (s >> 2) & 1, piece = (s & 3) ^ gswz(row & 15);
-    foff[u] = uint32_t(row * KC + h * 64 + piece * 16);
+    const int row = s >> 3, piece = (s & 7) ^ gswz(row & 15);
+    foff[u] = uint32_t(row * KC + piece * 16);
   }
   // Scale staging: thread tid < 256 carries the 8 scale bytes (blocks of the
   // step) of W row tid, the others those of X row tid - 256.
@@ -158,9 +166,10 @@ __global__ __launch_bounds__(kGWaves * 64) __attribute__((amdgpu_waves_per_eu(2)
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[j][i] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // per-lane LDS offsets: operand row 16t + r16, piece g4 of chunk h
-  const int w_lane = (128 * wn + r16) * 128 + 16 * (g4 ^ gswz(r16));
-  const int x_lane = (64 * wm + r16) * 128 + 16 * (g4 ^ gswz(r16));
+  // per-lane LDS offsets: operand row 16t + r16, piece 4h + g4
+  const int lsw = gswz(r16);
+  const int w_off0 = (128 * wn + r16) * 128 + 16 * (g4 ^ lsw), w_off1 = (128 * wn + r16) * 128 + 16 * ((4 + g4) ^ lsw);
+  const int x_off0 = (64 * wm + r16) * 128 + 16 * (g4 ^ lsw), x_off1 = (64 * wm + r16) * 128 + 16 * ((4 + g4) ^ lsw);
   const int ws_lane = (g4 * 16 + r16) * 16 + 8 * wn;
   const int xs_lane = (g4 * 16 + r16) * 16 + 4 * wm;
 
@@ -172,18 +181,23 @@ __global__ __launch_bounds__(kGWaves * 64) __attribute__((amdgpu_waves_per_eu(2)
       const uint32_t xsc = *reinterpret_cast<const uint32_t*>(&T.xsl[h][xs_lane]);
       uint4 xb[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xb[i] = *reinterpret_cast<const uint4*>(&T.x[x_lane + i * 16 * 128 + 64 * h]);
+      for (int i = 0; i < 4; ++i)
+        xb[i] = *reinterpret_cast<const uint4*>(&T.x[(h ? x_off1 : x_off0) + i * 16 * 128]);
 #define MXGEMM_ROW(j_)                                                                             \
       {                                                                                            \
-        const uint4 wa = *reinterpret_cast<const uint4*>(&T.w[w_lane + (j_) * 16 * 128 + 64 * h]); \
+        const uint4 wa = *reinterpret_cast<const uint4*>(&T.w[(h ? w_off1 : w_off0) + (j_) * 16 * 128]); \
         const int sa = int((j_) < 4 ? wsc.x : wsc.y);                                             \
         acc[j_][0] = mfma_fp4_16x16x128<(j_) & 3, 0>(wa, xb[0], acc[j_][0], sa, int(xsc));         \
         acc[j_][1] = mfma_fp4_16x16x128<(j_) & 3, 1>(wa, xb[1], acc[j_][1], sa, int(xsc));         \
         acc[j_][2] = mfma_fp4_16x16x128<(j_) & 3, 2>(wa, xb[2], acc[j_][2], sa, int(xsc));         \
         acc[j_][3] = mfma_fp4_16x16x128<(j_) & 3, 3>(wa, xb[3], acc[j_][3], sa, int(xsc));         \
       }
+      // MFMA issue at raised wave priority: a SIMD prefers the wave that is
+      // ready to feed the matrix core over one that is staging operands
+      __builtin_amdgcn_s_setprio(1);
       MXGEMM_ROW(0) MXGEMM_ROW(1) MXGEMM_ROW(2) MXGEMM_ROW(3)
       MXGEMM_ROW(4) MXGEMM_ROW(5) MXGEMM_ROW(6) MXGEMM_ROW(7)
+      __builtin_amdgcn_s_setprio(0);
 #undef MXGEMM_ROW
     }
   };
@@ -197,6 +211,8 @@ __global__ __launch_bounds__(kGWaves * 64) __attribute__((amdgpu_waves_per_eu(2)
   const std::integral_constant<int, 2> two_chunks;
   auto step = [&](int s, const GemmLds& cur, GemmLds& nxt) {
     issue(s + 1, nxt);
+    // keep the fills at the top of the step: they get the whole step to land
+    __builtin_amdgcn_sched_barrier(0);
     compute(cur, two_chunks);
     __builtin_amdgcn_sched_barrier(0);
     finish(nxt);
