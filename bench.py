@@ -383,8 +383,8 @@ def gemm_bench(args, dev):
     }
     if not args.no_cpu_baseline:
         import oracle
-        rows = np.sort(np.random.default_rng(13).choice(M, 2048, replace=False))
-        log("[bench] cpu baseline (oracle GEMM on 2048 rows)")
+        rows = np.sort(np.random.default_rng(13).choice(M, 8192, replace=False))
+        log("[bench] cpu baseline (oracle GEMM on 8192 rows)")
         t0 = time.perf_counter()
         ref = oracle.gemm_rows(x, w, M, N, K, mode, rows)
         dt = time.perf_counter() - t0
@@ -395,7 +395,7 @@ def gemm_bench(args, dev):
         result["cpu_baseline"] = {
             "value": 2.0 * rows.size * N * K / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle", "seconds": dt,
-            "sample": f"quantization of W and of 2048 seeded X rows, their exact product (numpy fp64), "
+            "sample": f"quantization of W and of 8192 seeded X rows, their exact product (numpy fp64), "
                       f"{dt:.1f} s; FLOP counted as 2*N*K per row",
             "max_diff_over_bound_on_sample": float((np.abs(got - ref["out"]) / (err + ulp)).max()),
         }
