@@ -86,6 +86,19 @@ int mxq_quantize(const void *x_bf16, int64_t batch, int64_t rows, int64_t cols, 
                  int mode, uint8_t *codes, uint8_t *scales, void *stream);
 
 /*
+ * mxq_quantize_strided -- mxq_quantize of a strided [B][H][rows][cols] view
+ * with contiguous columns: element (b, h, r, c) at x + b*strides[0] +
+ * h*strides[1] + r*strides[2] + c (elements; strides a host array of 3).
+ * Output: the canonical layout of mxq_quantize with batch = B*H, bit-identical
+ * to quantizing a dense copy.  Requires cols % 32 == 0, strides non-negative
+ * multiples of 8, x and codes 16-byte aligned, B*H <= 65535.
+ * Errors: MXQ_ERR_INVALID_ARG, MXQ_ERR_UNSUPPORTED, MXQ_ERR_HIP.
+ */
+int mxq_quantize_strided(const void *x_bf16, int64_t B, int64_t H, int64_t rows, int64_t cols,
+                         const int64_t *strides, int axis, int mode, uint8_t *codes, uint8_t *scales,
+                         void *stream);
+
+/*
  * mxattn_kv_tile -- number of keys per key tile of the attention kernel for
  * head dimension d (0 if d is unsupported).  The running row maximum is
  * updated once per key tile, in ascending key order, and the quantized
@@ -149,6 +162,23 @@ int mxattn_fwd_quantized(const uint8_t *qc, const uint8_t *qs, const uint8_t *kc
 int mxattn_fwd_kv_quantized(const void *q, const uint8_t *kc, const uint8_t *ks, const uint8_t *vc,
                             const uint8_t *vs, int64_t B, int64_t H, int64_t N, int64_t d, int mode,
                             int pnq, float softmax_scale, void *o, void *stream);
+
+/*
+ * mxattn_fwd_strided -- mxattn_fwd on strided views, for callers whose
+ * tensors are not dense [B][H][N][d]: element (b, h, n, c) of X (Q, K, V or
+ * O) sits at X + b*s[0] + h*s[1] + n*s[2] + c elements, with s = the
+ * tensor's three strides (host arrays of 3 int64, in elements; d is
+ * contiguous).  [B][N][H][d] (BNHD) is s = {N*H*d, d, H*d}; dense BHND is
+ * {H*N*d, N*d, d}; slices of a packed [B][N][3][H][d] QKV tensor work as
+ * they are.  Strides must be non-negative multiples of 8 (16-byte rows) and
+ * O must not overlap Q, K or V.  The result is bit-identical to mxattn_fwd
+ * on dense copies.  Workspace as mxattn_fwd (mxattn_workspace_bytes).
+ * Errors as mxattn_fwd; MXQ_ERR_UNSUPPORTED also when B*H > 65535.
+ */
+int mxattn_fwd_strided(const void *q, const void *k, const void *v, void *o, int64_t B, int64_t H,
+                       int64_t N, int64_t d, const int64_t *q_strides, const int64_t *k_strides,
+                       const int64_t *v_strides, const int64_t *o_strides, int mode, int pnq,
+                       float softmax_scale, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * mxgemm_quantized -- Y = X W^T on MXFP4 operands (the MXAttention abstract's

@@ -61,6 +61,11 @@ def lib() -> ctypes.CDLL:
     L.mxgemm_workspace_bytes.restype = ctypes.c_size_t
     L.mxgemm.argtypes = [P, P, P, i64, i64, i64, i32, P, P, ctypes.c_size_t, P]
     L.mxgemm.restype = i32
+    L.mxattn_fwd_strided.argtypes = [P, P, P, P, i64, i64, i64, i64, P, P, P, P, i32, i32, f32, P,
+                                     ctypes.c_size_t, P]
+    L.mxattn_fwd_strided.restype = i32
+    L.mxq_quantize_strided.argtypes = [P, i64, i64, i64, i64, P, i32, i32, P, P, P]
+    L.mxq_quantize_strided.restype = i32
     L.mxq_dump.argtypes = [ctypes.c_char_p, P, P, i64, i64, i64, i32, i32, P]
     L.mxq_dump.restype = i32
     _lib = L
@@ -69,7 +74,8 @@ def lib() -> ctypes.CDLL:
 
 EXPORTS = ("mxq_status_string", "mxattn_version", "mxq_quantize", "mxattn_kv_tile",
            "mxattn_workspace_bytes", "mxattn_fwd", "mxattn_fwd_quantized", "mxattn_fwd_kv_quantized",
-           "mxgemm_quantized", "mxgemm_workspace_bytes", "mxgemm", "mxq_dump")
+           "mxgemm_quantized", "mxgemm_workspace_bytes", "mxgemm", "mxattn_fwd_strided",
+           "mxq_quantize_strided", "mxq_dump")
 
 
 def status_string(status: int) -> str:
@@ -185,6 +191,53 @@ def fwd_kv_quantized(q, kc, ks, vc, vs, mode="uos", pnq: bool = True, softmax_sc
                                          float(softmax_scale), o.data_ptr(), _stream(q)),
            "mxattn_fwd_kv_quantized")
     return o
+
+
+def _strides3(t, what):
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError(f"{what} must be a [B, H, N, d]-shaped view with contiguous d")
+    return (ctypes.c_int64 * 3)(*t.stride()[:3])
+
+
+def fwd_strided(q, k, v, mode="uos", pnq: bool = True, softmax_scale: float = 0.0, out=None, workspace=None):
+    """mxattn_fwd on [B, H, N, d]-shaped views with any strides and contiguous
+    d, e.g. a [B, N, H, d] tensor seen through .transpose(1, 2), or slices of
+    a packed QKV tensor.  O gets q's strides when q is dense in some order
+    (torch.empty_like), else the dense [B, H, N, d] layout."""
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{n} must be bf16")
+    if q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k and v must have the same [B, H, N, d] shape")
+    B, H, N, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+        if out.stride(3) != 1:
+            out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    need = workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().mxattn_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, d,
+                                    _strides3(q, "q"), _strides3(k, "k"), _strides3(v, "v"), _strides3(out, "out"),
+                                    _mode(mode), int(bool(pnq)), float(softmax_scale), workspace.data_ptr(),
+                                    workspace.numel(), _stream(q)), "mxattn_fwd_strided")
+    return out
+
+
+def quantize_strided(x, mode="uos", axis: int = 1):
+    """mxq_quantize of a [B, H, rows, cols]-shaped view with contiguous cols
+    (cols % 32 == 0); returns canonical (codes, scales) with batch B*H."""
+    import torch
+    B, H, R, C = x.shape
+    L = C if axis == 1 else R
+    nv = R if axis == 1 else C
+    nb = (L + 31) // 32
+    codes = torch.empty(B * H * nv * nb * 16, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(B * H * nv * nb, dtype=torch.uint8, device=x.device)
+    _check(lib().mxq_quantize_strided(x.data_ptr(), B, H, R, C, _strides3(x, "x"), int(axis), _mode(mode),
+                                      codes.data_ptr(), scales.data_ptr(), _stream(x)), "mxq_quantize_strided")
+    return codes, scales
 
 
 def gemm_quantized(xc, xs, wc, ws, M: int, N: int, K: int, out=None):

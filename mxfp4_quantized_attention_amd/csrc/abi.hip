@@ -15,9 +15,13 @@
 namespace mxattn {
 hipError_t launch_quantize(const void* x, int64_t batch, int64_t rows, int64_t cols, int axis,
                            int mode, uint8_t* codes, uint8_t* scales, hipStream_t stream);
-hipError_t launch_attention(const uint16_t* q, const uint8_t* qc, const uint8_t* qs, const uint8_t* kc,
-                            const uint8_t* ks, const uint8_t* vc, const uint8_t* vs, int BH, int N, int d,
-                            int mode, bool pnq, float softmax_scale, uint16_t* o, hipStream_t stream);
+hipError_t launch_attention(const uint16_t* q, const int64_t* q_strides, const uint8_t* qc, const uint8_t* qs,
+                            const uint8_t* kc, const uint8_t* ks, const uint8_t* vc, const uint8_t* vs, int H,
+                            int BH, int N, int d, int mode, bool pnq, float softmax_scale, uint16_t* o,
+                            const int64_t* o_strides, hipStream_t stream);
+hipError_t launch_quantize_strided(const void* x, int64_t B, int64_t H, int64_t rows, int64_t cols, int64_t sb,
+                                   int64_t sh, int64_t sn, int axis, int mode, uint8_t* codes, uint8_t* scales,
+                                   hipStream_t stream);
 hipError_t launch_gemm(const uint8_t* xc, const uint8_t* xs, const uint8_t* wc, const uint8_t* ws, int M,
                        int N, int K, uint16_t* y, hipStream_t stream);
 }  // namespace mxattn
@@ -113,6 +117,21 @@ int mxq_quantize(const void* x_bf16, int64_t batch, int64_t rows, int64_t cols, 
                                             static_cast<hipStream_t>(stream)));
 }
 
+int mxq_quantize_strided(const void* x, int64_t B, int64_t H, int64_t rows, int64_t cols, const int64_t* strides,
+                         int axis, int mode, uint8_t* codes, uint8_t* scales, void* stream) {
+  if (B < 0 || H < 0 || rows < 0 || cols < 0 || (axis != 0 && axis != 1) || !valid_mode(mode) || !strides)
+    return MXQ_ERR_INVALID_ARG;
+  if (B == 0 || H == 0 || rows == 0 || cols == 0) return MXQ_OK;
+  if (!x || !codes || !scales) return MXQ_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(codes)) return MXQ_ERR_INVALID_ARG;
+  for (int i = 0; i < 3; ++i)
+    if (strides[i] < 0 || strides[i] % 8 != 0 || strides[i] > (int64_t(1) << 40)) return MXQ_ERR_INVALID_ARG;
+  if (cols % 32 != 0) return MXQ_ERR_UNSUPPORTED;
+  if (B * H > 65535 || rows > (int64_t(1) << 24) || cols > (int64_t(1) << 16)) return MXQ_ERR_UNSUPPORTED;
+  return hip_status(mxattn::launch_quantize_strided(x, B, H, rows, cols, strides[0], strides[1], strides[2], axis,
+                                                    mode, codes, scales, static_cast<hipStream_t>(stream)));
+}
+
 int mxattn_kv_tile(int64_t d) { return (d == 64 || d == 128) ? kKvTile : 0; }
 
 size_t mxattn_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
@@ -129,8 +148,8 @@ int mxattn_fwd_quantized(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc
   if (!qc || !qs || !kc || !ks || !vc || !vs || !o) return MXQ_ERR_INVALID_ARG;
   if (!aligned16(qc) || !aligned16(kc) || !aligned16(vc) || !aligned16(o)) return MXQ_ERR_INVALID_ARG;
   const float scale = softmax_scale > 0.f ? softmax_scale : float(1.0 / std::sqrt(double(d)));
-  return hip_status(mxattn::launch_attention(nullptr, qc, qs, kc, ks, vc, vs, int(B * H), int(N), int(d),
-                                             mode, pnq != 0, scale, static_cast<uint16_t*>(o),
+  return hip_status(mxattn::launch_attention(nullptr, nullptr, qc, qs, kc, ks, vc, vs, int(H), int(B * H), int(N),
+                                             int(d), mode, pnq != 0, scale, static_cast<uint16_t*>(o), nullptr,
                                              static_cast<hipStream_t>(stream)));
 }
 
@@ -143,9 +162,9 @@ int mxattn_fwd_kv_quantized(const void* q, const uint8_t* kc, const uint8_t* ks,
   if (!q || !kc || !ks || !vc || !vs || !o) return MXQ_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(kc) || !aligned16(vc) || !aligned16(o)) return MXQ_ERR_INVALID_ARG;
   const float scale = softmax_scale > 0.f ? softmax_scale : float(1.0 / std::sqrt(double(d)));
-  return hip_status(mxattn::launch_attention(static_cast<const uint16_t*>(q), nullptr, nullptr, kc, ks, vc, vs,
-                                             int(B * H), int(N), int(d), mode, pnq != 0, scale,
-                                             static_cast<uint16_t*>(o), static_cast<hipStream_t>(stream)));
+  return hip_status(mxattn::launch_attention(static_cast<const uint16_t*>(q), nullptr, nullptr, nullptr, kc, ks, vc,
+                                             vs, int(H), int(B * H), int(N), int(d), mode, pnq != 0, scale,
+                                             static_cast<uint16_t*>(o), nullptr, static_cast<hipStream_t>(stream)));
 }
 
 int mxattn_fwd(const void* q, const void* k, const void* v, int64_t B, int64_t H, int64_t N, int64_t d,
@@ -166,9 +185,42 @@ int mxattn_fwd(const void* q, const void* k, const void* v, int64_t B, int64_t H
   if (e == hipSuccess) e = mxattn::launch_quantize(v, BH, N, d, 0, mode, ws + w.vc, ws + w.vs, s);
   if (e != hipSuccess) return MXQ_ERR_HIP;
   const float scale = softmax_scale > 0.f ? softmax_scale : float(1.0 / std::sqrt(double(d)));
-  return hip_status(mxattn::launch_attention(static_cast<const uint16_t*>(q), nullptr, nullptr, ws + w.kc,
-                                             ws + w.ks, ws + w.vc, ws + w.vs, int(BH), int(N), int(d), mode,
-                                             pnq != 0, scale, static_cast<uint16_t*>(o), s));
+  return hip_status(mxattn::launch_attention(static_cast<const uint16_t*>(q), nullptr, nullptr, nullptr, ws + w.kc,
+                                             ws + w.ks, ws + w.vc, ws + w.vs, int(H), int(BH), int(N), int(d),
+                                             mode, pnq != 0, scale, static_cast<uint16_t*>(o), nullptr, s));
+}
+
+int mxattn_fwd_strided(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H, int64_t N,
+                       int64_t d, const int64_t* q_strides, const int64_t* k_strides, const int64_t* v_strides,
+                       const int64_t* o_strides, int mode, int pnq, float softmax_scale, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  int st = check_attn_sizes(B, H, N, d);
+  if (st != MXQ_OK) return st;
+  if (B * H > 65535) return MXQ_ERR_UNSUPPORTED;
+  if (!valid_mode(mode) || (pnq != 0 && pnq != 1) || !std::isfinite(softmax_scale)) return MXQ_ERR_INVALID_ARG;
+  if (!q || !k || !v || !o || !q_strides || !k_strides || !v_strides || !o_strides) return MXQ_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return MXQ_ERR_INVALID_ARG;
+  const int64_t* all[4] = {q_strides, k_strides, v_strides, o_strides};
+  for (const int64_t* sp : all)
+    for (int i = 0; i < 3; ++i)  // every row must start 16-byte aligned; no stride may overflow an offset
+      if (sp[i] < 0 || sp[i] % 8 != 0 || sp[i] > (int64_t(1) << 40)) return MXQ_ERR_INVALID_ARG;
+  const int64_t BH = B * H;
+  const WsLayout w = ws_layout(BH, N, d);
+  if (!workspace || workspace_bytes < w.total) return MXQ_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return MXQ_ERR_INVALID_ARG;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = mxattn::launch_quantize_strided(k, B, H, N, d, k_strides[0], k_strides[1], k_strides[2], 1, mode,
+                                                 ws + w.kc, ws + w.ks, s);
+  if (e == hipSuccess)
+    e = mxattn::launch_quantize_strided(v, B, H, N, d, v_strides[0], v_strides[1], v_strides[2], 0, mode,
+                                        ws + w.vc, ws + w.vs, s);
+  if (e != hipSuccess) return MXQ_ERR_HIP;
+  const float scale = softmax_scale > 0.f ? softmax_scale : float(1.0 / std::sqrt(double(d)));
+  return hip_status(mxattn::launch_attention(static_cast<const uint16_t*>(q), q_strides, nullptr, nullptr,
+                                             ws + w.kc, ws + w.ks, ws + w.vc, ws + w.vs, int(H), int(BH), int(N),
+                                             int(d), mode, pnq != 0, scale, static_cast<uint16_t*>(o), o_strides,
+                                             s));
 }
 
 size_t mxgemm_workspace_bytes(int64_t M, int64_t K) {

@@ -33,7 +33,7 @@
 namespace mxattn {
 
 struct AttnArgs {
-  const uint16_t* q;   // bf16 Q [BH][N][D] (in-kernel quantization), or null
+  const uint16_t* q;   // bf16 Q (in-kernel quantization; strided, see below), or null
   const uint8_t* qc;   // else Q codes and scales, blocks along d
   const uint8_t* qs;
   const uint8_t* kc;
@@ -41,6 +41,10 @@ struct AttnArgs {
   const uint8_t* vc;
   const uint8_t* vs;
   uint16_t* o;
+  // element strides of bf16 Q (when q is set) and of O: row (b, h, n) starts
+  // at b * sb + h * sh + n * sn; d is contiguous
+  int64_t q_sb, q_sh, q_sn, o_sb, o_sh, o_sn;
+  int H;        // heads (splits the batch-head index of a workgroup)
   int BH;       // batch * heads
   int N;        // tokens per head (queries = keys)
   int nbn;      // 32-key blocks per V channel, ceil(N / 32)
@@ -200,6 +204,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   if (lin >= a.BH * a.ntq) return;
   const int64_t bh = lin / a.ntq;
   const int qt = lin % a.ntq;
+  const int64_t hb = bh / a.H, hh = bh % a.H;
+  const int64_t qrow = hb * a.q_sb + hh * a.q_sh, orow0 = hb * a.o_sb + hh * a.o_sh;
 
   // wave index through readfirstlane: the compiler then keeps everything
   // derived from it (LDS fill destinations) in scalar registers
@@ -221,7 +227,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
     if (qi < N && g4 < DB) {
       const int64_t row = bh * N + qi;
       if constexpr (QBF16) {
-        const uint4* src = reinterpret_cast<const uint4*>(a.q + row * D + 32 * g4);
+        const uint4* src = reinterpret_cast<const uint4*>(a.q + qrow + qi * a.q_sn + 32 * g4);
         const uint4 x0 = src[0], x1 = src[1], x2 = src[2], x3 = src[3];
         const uint32_t amax = max(max(absmax8_bits(x0), absmax8_bits(x1)), max(absmax8_bits(x2), absmax8_bits(x3)));
         const int e = block_exp_bf16bits<MODE>(amax);
@@ -443,7 +449,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
     const float inv = 1.0f / l;
     const int qi = qt * kBR + wave * (kQG * 16) + g * 16 + r16;
     if (qi < N) {
-      uint16_t* orow = a.o + (bh * N + qi) * int64_t(D);
+      uint16_t* orow = a.o + orow0 + qi * a.o_sn;
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         const uint32_t b0 = f32_to_bf16_rne(O[g][ct][0] * inv), b1 = f32_to_bf16_rne(O[g][ct][1] * inv);
@@ -454,11 +460,19 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   }
 }
 
-hipError_t launch_attention(const uint16_t* q, const uint8_t* qc, const uint8_t* qs, const uint8_t* kc,
-                            const uint8_t* ks, const uint8_t* vc, const uint8_t* vs, int BH, int N, int d,
-                            int mode, bool pnq, float softmax_scale, uint16_t* o, hipStream_t stream) {
+hipError_t launch_attention(const uint16_t* q, const int64_t* q_strides, const uint8_t* qc, const uint8_t* qs,
+                            const uint8_t* kc, const uint8_t* ks, const uint8_t* vc, const uint8_t* vs, int H,
+                            int BH, int N, int d, int mode, bool pnq, float softmax_scale, uint16_t* o,
+                            const int64_t* o_strides, hipStream_t stream) {
   AttnArgs a;
   a.q = q; a.qc = qc; a.qs = qs; a.kc = kc; a.ks = ks; a.vc = vc; a.vs = vs; a.o = o;
+  // null strides: dense [B][H][N][d]
+  const int64_t dense[3] = {int64_t(H) * N * d, int64_t(N) * d, d};
+  const int64_t* qst = q_strides ? q_strides : dense;
+  const int64_t* ost = o_strides ? o_strides : dense;
+  a.q_sb = qst[0]; a.q_sh = qst[1]; a.q_sn = qst[2];
+  a.o_sb = ost[0]; a.o_sh = ost[1]; a.o_sn = ost[2];
+  a.H = H;
   a.BH = BH;
   a.N = N;
   a.nbn = (N + 31) / 32;

@@ -19,6 +19,15 @@ typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 }  // namespace
 
+// Where the batch entries and rows of a [batch][rows][cols] input sit when it
+// is a strided view with contiguous columns: entry bi = (bi / H, bi % H)
+// starts at sb * (bi / H) + sh * (bi % H) elements and its rows are sn apart.
+// The dense layout is H = 1, sb = rows * cols, sn = cols.
+struct Layout3 {
+  int64_t H, sb, sh, sn;
+  __device__ __forceinline__ int64_t base(int64_t bi) const { return (bi / H) * sb + (bi % H) * sh; }
+};
+
 // Flat stream of full 32-element blocks: block i = elements [32i, 32i + 32)
 // of x, codes [16i, 16i + 16), scale [i].  Four lanes share a block (16 bytes
 // of input each), so a wave reads 1 KiB and writes 256 code bytes per step,
@@ -86,6 +95,46 @@ __global__ __launch_bounds__(256) void quant_rows_general_kernel(const uint16_t*
   scales[b] = uint8_t(e + 127);
 }
 
+// Blocks along the contiguous axis of a strided view (cols % 32 == 0): batch
+// entry blockIdx.y, 16-byte pieces of its rows walked with a grid stride
+// along x, four lanes per block as in the stream kernel.
+template <int MODE, int U>
+__global__ __launch_bounds__(256) void quant_rows_strided_kernel(const uint16_t* __restrict__ x,
+                                                                 uint32_t* __restrict__ codes,
+                                                                 uint8_t* __restrict__ scales, int64_t rows,
+                                                                 int64_t cols, Layout3 in) {
+  const int64_t bi = blockIdx.y;
+  const uint16_t* xb = x + in.base(bi);
+  const uint32_t ppr = uint32_t(cols / 8);            // 16-byte pieces per row
+  const uint32_t np = uint32_t(rows) * ppr;           // pieces in this entry
+  const int64_t out0 = bi * int64_t(rows) * (cols / 8);  // code dwords before this entry
+  const uint32_t step = gridDim.x * 256 * U;
+  for (uint32_t base = blockIdx.x * 256 * U + threadIdx.x; base < np; base += step) {
+    v4u v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t q = base + u * 256;
+      const uint32_t r = q / ppr, pc = q - r * ppr;
+      v[u] = q < np ? __builtin_nontemporal_load(reinterpret_cast<const v4u*>(xb + int64_t(r) * in.sn + pc * 8))
+                    : v4u{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t q = base + u * 256;
+      const uint4 w = make_uint4(v[u].x, v[u].y, v[u].z, v[u].w);
+      uint32_t m = absmax8_bits(w);
+      m = max(m, uint32_t(__builtin_amdgcn_mov_dpp(int(m), 0xB1, 0xF, 0xF, true)));
+      m = max(m, uint32_t(__builtin_amdgcn_mov_dpp(int(m), 0x4E, 0xF, 0xF, true)));
+      const int e = block_exp_bf16bits<MODE>(m);
+      const uint32_t c = encode8_bf16(w, e);
+      if (q < np) {
+        __builtin_nontemporal_store(c, codes + out0 + q);
+        if ((q & 3) == 0) scales[(out0 + q) >> 2] = uint8_t(e + 127);
+      }
+    }
+  }
+}
+
 // Blocks along rows (axis 0).  Work item = a 256-row x 64-column bf16 tile
 // of one batch entry; each workgroup walks items with a grid stride and
 // holds the next item's loads in registers while it encodes the current one
@@ -98,23 +147,24 @@ template <int MODE>
 __global__ __launch_bounds__(256) void quant_cols_kernel(const uint16_t* __restrict__ x,
                                                          uint8_t* __restrict__ codes,
                                                          uint8_t* __restrict__ scales, int64_t rows,
-                                                         int64_t cols, int64_t nb, int64_t ntc, int64_t nitems) {
+                                                         int64_t cols, int64_t nb, int64_t ntc, int64_t nitems,
+                                                         Layout3 in) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[256 * 64];
   const int tid = threadIdx.x;
   const int ntr = int((rows + 255) / 256);
-  const bool vec8 = (cols & 7) == 0;
+  const bool vec8 = (cols & 7) == 0 && (in.sn & 7) == 0;
   v4u buf[8];
   auto load = [&](int64_t item) {
     const int64_t bi = item / (int64_t(ntr) * ntc), rest = item % (int64_t(ntr) * ntc);
     const int64_t r0 = (rest / ntc) * 256, c0 = (rest % ntc) * 64;
-    const uint16_t* xb = x + bi * rows * cols;
+    const uint16_t* xb = x + in.base(bi);
     const int cc = (tid & 7) * 8;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int rr = (tid >> 3) + 32 * i;
       buf[i] = v4u{0, 0, 0, 0};
       if (r0 + rr < rows && c0 + cc < cols)
-        buf[i] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(xb + (r0 + rr) * cols + c0 + cc));
+        buf[i] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(xb + (r0 + rr) * in.sn + c0 + cc));
     }
   };
   int64_t item = blockIdx.x;
@@ -131,11 +181,11 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const uint16_t* __restr
         *reinterpret_cast<v4u*>(&tile[rr * 64 + (cc ^ (8 * i))]) = buf[i];
       }
     } else {
-      const uint16_t* xb = x + bi * rows * cols;
+      const uint16_t* xb = x + in.base(bi);
       for (int i = tid; i < 256 * 64; i += 256) {
         const int rr = i >> 6, cc = i & 63;
         tile[rr * 64 + (cc ^ (8 * (rr >> 5)))] =
-            (r0 + rr < rows && c0 + cc < cols) ? xb[(r0 + rr) * cols + c0 + cc] : uint16_t(0);
+            (r0 + rr < rows && c0 + cc < cols) ? xb[(r0 + rr) * in.sn + c0 + cc] : uint16_t(0);
       }
     }
     __syncthreads();
@@ -205,12 +255,51 @@ hipError_t launch_quantize(const void* x, int64_t batch, int64_t rows, int64_t c
     const int64_t ntr = (rows + 255) / 256, ntc = (cols + 63) / 64;
     const int64_t nitems = batch * ntr * ntc;
     const int64_t grid = nitems < kColsGrid ? nitems : kColsGrid;
+    const Layout3 dense{1, rows * cols, 0, cols};
     if (mode == kModeUOS)
       quant_cols_kernel<kModeUOS><<<dim3(unsigned(grid)), dim3(256), 0, stream>>>(static_cast<const uint16_t*>(x),
-                                                                   codes, scales, rows, cols, nb, ntc, nitems);
+                                                                   codes, scales, rows, cols, nb, ntc, nitems, dense);
     else
       quant_cols_kernel<kModeOCP><<<dim3(unsigned(grid)), dim3(256), 0, stream>>>(static_cast<const uint16_t*>(x),
-                                                                   codes, scales, rows, cols, nb, ntc, nitems);
+                                                                   codes, scales, rows, cols, nb, ntc, nitems, dense);
+  }
+  return hipGetLastError();
+}
+
+// Quantization of a strided [B][H][rows][cols] view with contiguous columns
+// (element (b, h, r, c) at x + b sb + h sh + r sn + c) into the canonical
+// dense output of batch B * H.  Requires cols % 32 == 0 and, for loads of
+// 16 bytes, sb, sh, sn multiples of 8 and x 16-byte aligned (the caller
+// checks); B * H <= 65535.
+hipError_t launch_quantize_strided(const void* x, int64_t B, int64_t H, int64_t rows, int64_t cols, int64_t sb,
+                                   int64_t sh, int64_t sn, int axis, int mode, uint8_t* codes, uint8_t* scales,
+                                   hipStream_t stream) {
+  if (B == 0 || H == 0 || rows == 0 || cols == 0) return hipSuccess;
+  const Layout3 in{H, sb, sh, sn};
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+  if (axis == 1) {
+    constexpr int U = 4;
+    const int64_t np = rows * (cols / 8);
+    int64_t gx = (np + 256 * U - 1) / (256 * U);
+    if (gx > 1024) gx = 1024;
+    const dim3 grid(unsigned(gx), unsigned(B * H));
+    if (mode == kModeUOS)
+      quant_rows_strided_kernel<kModeUOS, U><<<grid, dim3(256), 0, stream>>>(xp, reinterpret_cast<uint32_t*>(codes),
+                                                                             scales, rows, cols, in);
+    else
+      quant_rows_strided_kernel<kModeOCP, U><<<grid, dim3(256), 0, stream>>>(xp, reinterpret_cast<uint32_t*>(codes),
+                                                                             scales, rows, cols, in);
+  } else {
+    const int64_t nb = (rows + 31) / 32;
+    const int64_t ntr = (rows + 255) / 256, ntc = (cols + 63) / 64;
+    const int64_t nitems = B * H * ntr * ntc;
+    const int64_t grid = nitems < kColsGrid ? nitems : kColsGrid;
+    if (mode == kModeUOS)
+      quant_cols_kernel<kModeUOS><<<dim3(unsigned(grid)), dim3(256), 0, stream>>>(xp, codes, scales, rows, cols, nb,
+                                                                                   ntc, nitems, in);
+    else
+      quant_cols_kernel<kModeOCP><<<dim3(unsigned(grid)), dim3(256), 0, stream>>>(xp, codes, scales, rows, cols, nb,
+                                                                                   ntc, nitems, in);
   }
   return hipGetLastError();
 }

@@ -100,6 +100,31 @@ def test_attention_argument_errors():
     assert kvq(A, A, A, A, A, 1, 1, 64, 128, 1, 1, float("inf"), A, None) == INVALID
 
 
+def test_strided_argument_errors():
+    import ctypes
+    L = mx.lib()
+    A = 1 << 20
+    s3 = lambda a, b, c: (ctypes.c_int64 * 3)(a, b, c)
+    good = s3(4 * 64 * 128, 128, 4 * 128)  # [B][N][H][d] with H=4, N=64, d=128 seen as B,H,N
+
+    def fwd(qs=good, ks=good, vs=good, os_=good, B=1, H=4, N=64, d=128, ws=A, wsb=1 << 40, o=A):
+        return L.mxattn_fwd_strided(A, A, A, o, B, H, N, d, qs, ks, vs, os_, 1, 1, 0.0, ws, wsb, None)
+
+    assert fwd(qs=None) == INVALID
+    assert fwd(os_=s3(8, 8, 4)) == INVALID          # not a multiple of 8 elements
+    assert fwd(ks=s3(-8, 8, 8)) == INVALID         # negative
+    assert fwd(o=A + 2) == INVALID
+    assert fwd(d=96) == UNSUPPORTED
+    assert fwd(B=300, H=300) == UNSUPPORTED        # B*H > 65535
+    assert fwd(ws=None) == WORKSPACE
+    q = L.mxq_quantize_strided
+    assert q(A, 1, 1, 64, 128, None, 1, 1, A, A, None) == INVALID
+    assert q(A, 1, 1, 64, 128, s3(0, 0, 12), 1, 1, A, A, None) == INVALID
+    assert q(A, 1, 1, 64, 96 + 8, s3(0, 0, 104), 1, 1, A, A, None) == UNSUPPORTED  # cols % 32
+    assert q(A, 1, 1, 64, 128, s3(0, 0, 128), 2, 1, A, A, None) == INVALID       # axis
+    assert q(None, 0, 1, 64, 128, s3(0, 0, 128), 1, 1, None, None, None) == OK   # empty: no-op
+
+
 def test_dump_from_host_memory(tmp_path):
     import oracle
     import workloads
