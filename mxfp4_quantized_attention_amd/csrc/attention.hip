@@ -285,20 +285,28 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
     voff[u] = (row * nbn + ((slot & 3) ^ v_swz(row))) * 16;
   }
   // Scale staging.  Thread tid < kBC carries the DB scale bytes of key kb + tid
-  // (one load), thread tid < 4 D one V scale byte (channel tid % D, block
-  // tid / D of the tile); both go to the lane-ordered layout: byte b of key
-  // tid to ks[(16 b + r) * 8 + t], byte b of channel 16 ct + r to
-  // vs[(16 b + r) * 8 + ct] (vs follows ks, so one offset from ks serves both).
-  static_assert(4 * D <= NT, "one V scale byte per thread");
+  // (one load); the 4 D V scale bytes of the tile (item it: channel it % D,
+  // block it / D) go VB per thread, items tid + NT v.  Both go to the
+  // lane-ordered layout: byte b of key tid to ks[(16 b + r) * 8 + t], byte b
+  // of channel 16 ct + r to vs[(16 b + r) * 8 + ct] (vs follows ks, so one
+  // offset from ks serves both).
+  static_assert(kBC <= NT, "one K scale word per thread");
+  constexpr int VB = (4 * D + NT - 1) / NT;
   const int kdst = ((((tid >> 5) << 2) | (tid & 3)) * 8) + ((tid & 31) >> 2);
-  const int vch = tid % D, vblk = tid / D;
-  const int vdst = 64 * 8 + (vch & 15) * 8 + (vch >> 4) + 128 * vblk;
-  // Threads with no byte to carry load from an offset past every record
+  // Threads with nothing to carry load from an offset past every record
   // count: the range check returns zero without touching memory, and every
   // thread runs the same instructions.
   const uint32_t kso = tid < kBC ? uint32_t(tid * DB) : 0x7FFFFFF0u;
-  const uint32_t vso = tid < 4 * D ? uint32_t(vch * nbn + vblk) : 0x7FFFFFF0u;
-  uint32_t kreg = 0, vreg = 0;
+  int vdst[VB];
+  uint32_t vso[VB], vreg[VB];
+#pragma unroll
+  for (int v = 0; v < VB; ++v) {
+    const int it = tid + NT * v, vch = it % D, vblk = it / D;
+    vdst[v] = 64 * 8 + (vch & 15) * 8 + (vch >> 4) + 128 * vblk;
+    vso[v] = it < 4 * D ? uint32_t(vch * nbn + vblk) : 0x7FFFFFF0u;
+    vreg[v] = 0;
+  }
+  uint32_t kreg = 0;
 
   // Every fill is a raw buffer load whose descriptor starts at the tile's
   // first byte and whose record count is the bytes left in the head, so the
@@ -319,7 +327,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
         (void*)(vs_h + vb0), 0, vshead - vb0, kBufferFlags);
     if constexpr (DB == 4) kreg = __builtin_amdgcn_raw_buffer_load_b32(ksrs, kso, 0, 0);
     else kreg = __builtin_amdgcn_raw_buffer_load_b16(ksrs, kso, 0, 0);
-    vreg = __builtin_amdgcn_raw_buffer_load_b8(vsrs, vso, 0, 0);
+#pragma unroll
+    for (int v = 0; v < VB; ++v) vreg[v] = __builtin_amdgcn_raw_buffer_load_b8(vsrs, vso[v], 0, 0);
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(kc_h + int64_t(kb) * CROW), 0, khead - kb * CROW, kBufferFlags);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
@@ -340,7 +349,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
 #pragma unroll
       for (int b = 0; b < DB; ++b) T.ks[kdst + 128 * b] = uint8_t(kreg >> (8 * b));
     }
-    if (4 * D == NT || tid < 4 * D) T.ks[vdst] = uint8_t(vreg);
+#pragma unroll
+    for (int v = 0; v < VB; ++v)
+      if (4 * D >= NT * (v + 1) || tid + NT * v < 4 * D) T.ks[vdst[v]] = uint8_t(vreg[v]);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's LDS fills have landed
   };
 
