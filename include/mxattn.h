@@ -181,6 +181,44 @@ int mxattn_fwd_strided(const void *q, const void *k, const void *v, void *o, int
                        float softmax_scale, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * mxattn_varlen_workspace_bytes -- bytes of device workspace mxattn_fwd_varlen
+ * needs for `batch` sequences over T tokens (0 on bad sizes): K codes and
+ * scales [H][T], V codes and scales [H][d][ceil(T/32) + batch blocks], and a
+ * table of 4 (batch + 1) ints built from cu_seqlens.
+ */
+size_t mxattn_varlen_workspace_bytes(int64_t batch, int64_t T, int64_t H, int64_t d);
+
+/*
+ * mxattn_fwd_varlen -- mxattn_fwd over a batch of sequences of different
+ * lengths packed along one token axis (the variable-length layout of DiT and
+ * LLM pipelines).  Sequence s holds tokens [cu_seqlens[s], cu_seqlens[s+1]);
+ * every sequence is its own non-causal attention problem, computed exactly
+ * as mxattn_fwd would compute it alone (same K/V quantization along d and
+ * along the sequence's own tokens, 32-token V blocks starting at the
+ * sequence's first token, same key tiles), so the result is bit-identical to
+ * one mxattn_fwd call per sequence.
+ * q, k, v, o: bf16, element (t, h, c) of X at X + t*s_tok + h*s_head + c,
+ *   with strides = {q_tok, q_head, k_tok, k_head, v_tok, v_head, o_tok,
+ *   o_head} (host array of 8 int64, elements; non-negative multiples of 8),
+ *   or strides = NULL for packed [T][H][d] (s_tok = H*d, s_head = d).
+ * cu_seqlens: device array of batch + 1 int32 prefix offsets, 4-byte
+ *   aligned, expected non-decreasing from 0 to T.  The kernels read it
+ *   clamped to [0, T] and made non-decreasing, so a malformed array gives
+ *   wrong results, never an access outside the tensors; tokens outside every
+ *   sequence are not written.
+ * batch >= 1, T >= 0 (T = 0 does nothing), H >= 1, d in {64, 128}.
+ * workspace: at least mxattn_varlen_workspace_bytes(batch, T, H, d).
+ * Other arguments as mxattn_fwd.
+ * Errors: MXQ_ERR_INVALID_ARG (null or misaligned pointer, bad sizes, mode,
+ * pnq or strides), MXQ_ERR_UNSUPPORTED (d, or batch > 2^20, T > 2^24,
+ * H > 65535, or sizes past the 32-bit offsets of the kernels),
+ * MXQ_ERR_WORKSPACE, MXQ_ERR_HIP.
+ */
+int mxattn_fwd_varlen(const void *q, const void *k, const void *v, void *o, const int32_t *cu_seqlens,
+                      int64_t batch, int64_t T, int64_t H, int64_t d, const int64_t *strides, int mode,
+                      int pnq, float softmax_scale, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * mxgemm_quantized -- Y = X W^T on MXFP4 operands (the MXAttention abstract's
  * UOS is data-free, so the same quantizer serves the linear layers around
  * attention).  X [M][K] and W [N][K] are quantized along K in the canonical

@@ -68,6 +68,10 @@ def lib() -> ctypes.CDLL:
     L.mxq_quantize_strided.restype = i32
     L.mxq_dump.argtypes = [ctypes.c_char_p, P, P, i64, i64, i64, i32, i32, P]
     L.mxq_dump.restype = i32
+    L.mxattn_varlen_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    L.mxattn_varlen_workspace_bytes.restype = ctypes.c_size_t
+    L.mxattn_fwd_varlen.argtypes = [P, P, P, P, P, i64, i64, i64, i64, P, i32, i32, f32, P, ctypes.c_size_t, P]
+    L.mxattn_fwd_varlen.restype = i32
     _lib = L
     return L
 
@@ -75,7 +79,7 @@ def lib() -> ctypes.CDLL:
 EXPORTS = ("mxq_status_string", "mxattn_version", "mxq_quantize", "mxattn_kv_tile",
            "mxattn_workspace_bytes", "mxattn_fwd", "mxattn_fwd_quantized", "mxattn_fwd_kv_quantized",
            "mxgemm_quantized", "mxgemm_workspace_bytes", "mxgemm", "mxattn_fwd_strided",
-           "mxq_quantize_strided", "mxq_dump")
+           "mxq_quantize_strided", "mxq_dump", "mxattn_varlen_workspace_bytes", "mxattn_fwd_varlen")
 
 
 def status_string(status: int) -> str:
@@ -222,6 +226,46 @@ def fwd_strided(q, k, v, mode="uos", pnq: bool = True, softmax_scale: float = 0.
                                     _strides3(q, "q"), _strides3(k, "k"), _strides3(v, "v"), _strides3(out, "out"),
                                     _mode(mode), int(bool(pnq)), float(softmax_scale), workspace.data_ptr(),
                                     workspace.numel(), _stream(q)), "mxattn_fwd_strided")
+    return out
+
+
+def varlen_workspace_bytes(batch: int, T: int, H: int, d: int) -> int:
+    return int(lib().mxattn_varlen_workspace_bytes(batch, T, H, d))
+
+
+def fwd_varlen(q, k, v, cu_seqlens, mode="uos", pnq: bool = True, softmax_scale: float = 0.0, out=None,
+               workspace=None):
+    """mxattn_fwd_varlen on [T, H, d]-shaped views (token and head strides
+    free, d contiguous) with cu_seqlens an int32 device tensor of batch + 1
+    prefix offsets.  Each sequence attends to itself only; the result equals
+    one mxattn_fwd call per sequence, bit for bit.  O is allocated like q
+    (tokens outside every sequence are left as allocated) unless given."""
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{n} must be bf16")
+        if t.dim() != 3 or t.stride(2) != 1:
+            raise ValueError(f"{n} must be a [T, H, d]-shaped view with contiguous d")
+    if q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k and v must have the same [T, H, d] shape")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous 1-D int32 tensor")
+    if cu_seqlens.device != q.device:
+        raise ValueError("cu_seqlens must be on q's device")
+    T, H, d = q.shape
+    batch = cu_seqlens.numel() - 1
+    if out is None:
+        out = torch.empty_like(q)
+        if out.stride(2) != 1:
+            out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    need = varlen_workspace_bytes(batch, T, H, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = (ctypes.c_int64 * 8)(q.stride(0), q.stride(1), k.stride(0), k.stride(1), v.stride(0), v.stride(1),
+                              out.stride(0), out.stride(1))
+    _check(lib().mxattn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), cu_seqlens.data_ptr(),
+                                   batch, T, H, d, st, _mode(mode), int(bool(pnq)), float(softmax_scale),
+                                   workspace.data_ptr(), workspace.numel(), _stream(q)), "mxattn_fwd_varlen")
     return out
 
 

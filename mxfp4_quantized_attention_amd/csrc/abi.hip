@@ -24,6 +24,14 @@ hipError_t launch_quantize_strided(const void* x, int64_t B, int64_t H, int64_t 
                                    hipStream_t stream);
 hipError_t launch_gemm(const uint8_t* xc, const uint8_t* xs, const uint8_t* wc, const uint8_t* ws, int M,
                        int N, int K, uint16_t* y, hipStream_t stream);
+hipError_t launch_varlen_table(const int* cu_seqlens, int batch, int T, int* tab, hipStream_t stream);
+hipError_t launch_quantize_varlen_cols(const void* x, int batch, int64_t T, int64_t H, int64_t d, int64_t sh,
+                                       int64_t sn, const int* tab, int mode, uint8_t* codes, uint8_t* scales,
+                                       hipStream_t stream);
+hipError_t launch_attention_varlen(const uint16_t* q, int64_t q_sn, int64_t q_sh, const uint8_t* kc,
+                                   const uint8_t* ks, const uint8_t* vc, const uint8_t* vs, const int* tab,
+                                   int batch, int T, int H, int d, int mode, bool pnq, float softmax_scale,
+                                   uint16_t* o, int64_t o_sn, int64_t o_sh, hipStream_t stream);
 }  // namespace mxattn
 
 namespace {
@@ -69,6 +77,42 @@ int check_attn_sizes(int64_t B, int64_t H, int64_t N, int64_t d) {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MXQ_OK : MXQ_ERR_HIP; }
+
+// Varlen workspace: K codes/scales [H][T], V codes/scales sized for
+// [H][d][vstride] with vstride = ceil(T / 32) + batch blocks per channel (an
+// upper bound on the blocks of all sequences, each padded to 32 tokens; the
+// kernels use the exact count from the table), then the varlen table,
+// 4 (batch + 1) ints.
+struct VarlenLayout {
+  size_t kc, ks, vc, vs, tab, total;
+  int64_t vstride;
+};
+
+VarlenLayout varlen_layout(int64_t batch, int64_t T, int64_t H, int64_t d) {
+  VarlenLayout w;
+  w.vstride = (T + 31) / 32 + batch;
+  size_t off = 0;
+  w.kc = off; off = round256(off + size_t(H * T * d / 2));
+  w.ks = off; off = round256(off + size_t(H * T * (d / 32)));
+  w.vc = off; off = round256(off + size_t(H * d * w.vstride * 16));
+  w.vs = off; off = round256(off + size_t(H * d * w.vstride));
+  w.tab = off; off = round256(off + size_t(4 * (batch + 1)) * sizeof(int));
+  w.total = off;
+  return w;
+}
+
+int check_varlen_sizes(int64_t batch, int64_t T, int64_t H, int64_t d) {
+  if (batch < 1 || T < 0 || H < 1) return MXQ_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return MXQ_ERR_UNSUPPORTED;
+  if (batch > (int64_t(1) << 20) || T > (int64_t(1) << 24) || H > 65535) return MXQ_ERR_UNSUPPORTED;
+  // V block offsets of one head (d channels of vstride blocks, 16 bytes each)
+  // are 32-bit in the kernels, and so is the workgroup count
+  const int64_t vstride = (T + 31) / 32 + batch;
+  if (d * vstride * 16 > (int64_t(1) << 31) - 1) return MXQ_ERR_UNSUPPORTED;
+  if (H * T * d > kMaxAttnElems) return MXQ_ERR_UNSUPPORTED;
+  if (H * ((T + 127) / 128 + batch) + 8 > (int64_t(1) << 31) - 1) return MXQ_ERR_UNSUPPORTED;
+  return MXQ_OK;
+}
 
 int check_gemm_sizes(int64_t M, int64_t N, int64_t K) {
   if (M < 1 || N < 1 || K < 1) return MXQ_ERR_INVALID_ARG;
@@ -221,6 +265,46 @@ int mxattn_fwd_strided(const void* q, const void* k, const void* v, void* o, int
                                              ws + w.kc, ws + w.ks, ws + w.vc, ws + w.vs, int(H), int(BH), int(N),
                                              int(d), mode, pnq != 0, scale, static_cast<uint16_t*>(o), o_strides,
                                              s));
+}
+
+size_t mxattn_varlen_workspace_bytes(int64_t batch, int64_t T, int64_t H, int64_t d) {
+  if (check_varlen_sizes(batch, T, H, d) != MXQ_OK) return 0;
+  return varlen_layout(batch, T, H, d).total;
+}
+
+int mxattn_fwd_varlen(const void* q, const void* k, const void* v, void* o, const int32_t* cu_seqlens,
+                      int64_t batch, int64_t T, int64_t H, int64_t d, const int64_t* strides, int mode, int pnq,
+                      float softmax_scale, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_varlen_sizes(batch, T, H, d);
+  if (st != MXQ_OK) return st;
+  if (!valid_mode(mode) || (pnq != 0 && pnq != 1) || !std::isfinite(softmax_scale)) return MXQ_ERR_INVALID_ARG;
+  if (T == 0) return MXQ_OK;
+  if (!q || !k || !v || !o || !cu_seqlens) return MXQ_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return MXQ_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) return MXQ_ERR_INVALID_ARG;
+  // token and head strides of Q, K, V, O (elements); null: packed [T][H][d]
+  const int64_t packed[8] = {H * d, d, H * d, d, H * d, d, H * d, d};
+  const int64_t* sp = strides ? strides : packed;
+  for (int i = 0; i < 8; ++i)
+    if (sp[i] < 0 || sp[i] % 8 != 0 || sp[i] > (int64_t(1) << 40)) return MXQ_ERR_INVALID_ARG;
+  const VarlenLayout w = varlen_layout(batch, T, H, d);
+  if (!workspace || workspace_bytes < w.total) return MXQ_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return MXQ_ERR_INVALID_ARG;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  int* tab = reinterpret_cast<int*>(ws + w.tab);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = mxattn::launch_varlen_table(cu_seqlens, int(batch), int(T), tab, s);
+  if (e == hipSuccess)
+    e = mxattn::launch_quantize_strided(k, 1, H, T, d, 0, sp[3], sp[2], 1, mode, ws + w.kc, ws + w.ks, s);
+  if (e == hipSuccess)
+    e = mxattn::launch_quantize_varlen_cols(v, int(batch), T, H, d, sp[5], sp[4], tab, mode, ws + w.vc, ws + w.vs,
+                                            s);
+  if (e != hipSuccess) return MXQ_ERR_HIP;
+  const float scale = softmax_scale > 0.f ? softmax_scale : float(1.0 / std::sqrt(double(d)));
+  return hip_status(mxattn::launch_attention_varlen(static_cast<const uint16_t*>(q), sp[0], sp[1], ws + w.kc,
+                                                    ws + w.ks, ws + w.vc, ws + w.vs, tab, int(batch), int(T), int(H),
+                                                    int(d), mode, pnq != 0, scale, static_cast<uint16_t*>(o), sp[6],
+                                                    sp[7], s));
 }
 
 size_t mxgemm_workspace_bytes(int64_t M, int64_t K) {

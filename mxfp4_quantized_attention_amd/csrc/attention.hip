@@ -46,11 +46,18 @@ struct AttnArgs {
   int64_t q_sb, q_sh, q_sn, o_sb, o_sh, o_sn;
   int H;        // heads (splits the batch-head index of a workgroup)
   int BH;       // batch * heads
-  int N;        // tokens per head (queries = keys)
-  int nbn;      // 32-key blocks per V channel, ceil(N / 32)
+  int N;        // tokens per head (queries = keys); varlen: unused
+  int vcs;      // V channel stride in 32-key blocks (dense: ceil(N / 32); varlen: from the table)
   int ntq;      // query tiles per head
   int per_xcd;  // workgroups per XCD in the tile order below
   float c;      // softmax_scale * log2(e)
+  // varlen batches (packed [T][H][d] tokens): the table of sequence starts,
+  // query-tile and V-block prefixes (4 (batch + 1) ints, built on the
+  // device), the number of sequences, and T, the K code rows per head.
+  // Workgroups then run over (head, query tile of any sequence).
+  const int* vl;
+  int batch;
+  int kts;
 };
 
 constexpr int kBC = 128;    // keys per tile: the running-max update granularity
@@ -90,18 +97,22 @@ __device__ __forceinline__ float sum_over_blocks(float x) {
 
 // LDS layout of one 128-key tile.  K codes [key][64 B] and V codes
 // [channel][64 B] (the tile's four 32-key blocks), 16-byte chunks XOR-swizzled
-// so the rows read by one MFMA operand load hit distinct banks, whether the LDS
-// serves 8 lanes from 32 banks or 16 lanes from 64 banks per cycle; the
-// swizzle term of a lane does not change from one sub-tile to the next.
+// by row.  The operand reads of both MFMAs touch rows whose offsets differ in
+// bits the swizzle does not look at (K: key rows 4t apart; V: channel rows 16
+// ct apart), so a lane's swizzle term is the same for every sub-tile.  The
+// swizzle functions were chosen by measurement (SQ_LDS_BANK_CONFLICT for every
+// XOR swizzle of this access shape on gfx950): a ds_read_b128 wave is served
+// bank-conflict-free when the chunk flips with bit 2 of the lane's row index
+// within its 16-row group (K: key-row bit 5; V: channel-row bit 2), and the
+// previous swizzles, which also folded bit 3 into the low chunk bit, cost
+// about 3.9 conflict cycles per read.
 // Scales are stored in MFMA lane order, 8 bytes per lane: ks[lane][t] is the
 // K scale of sub-tile t (key row of that lane in sub-tile t, d-block l/16),
 // vs[lane][ct] the V scale of channel tile ct (channel 16 ct + l%16, block
 // l/16); one 8-byte read per lane fetches all of them and the MFMA's op_sel
 // picks the byte.
-__device__ __forceinline__ int k_swz(int row) { return ((row >> 5) & 3) ^ (row & 2); }
-__device__ __forceinline__ int v_swz(int row) { return ((row >> 2) & 3) ^ (row & 2); }
-__device__ __forceinline__ int k_chunk_addr(int row, int c) { return row * 64 + 16 * (c ^ k_swz(row)); }
-__device__ __forceinline__ int v_chunk_addr(int row, int c) { return row * 64 + 16 * (c ^ v_swz(row)); }
+__device__ __forceinline__ int k_swz(int row) { return ((row >> 1) & 1) | ((row >> 4) & 2); }
+__device__ __forceinline__ int v_swz(int row) { return (row >> 1) & 3; }
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
@@ -183,7 +194,7 @@ __device__ __forceinline__ void softmax_group(v4f (&S)[8], float& m, float c, ui
 
 }  // namespace
 
-template <int D, int MODE, bool PNQ, bool QBF16>
+template <int D, int MODE, bool PNQ, bool QBF16, bool VARLEN>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void attn_fwd_kernel(AttnArgs a) {
   constexpr int DB = D / 32;      // 32-blocks along d in a Q/K row
   constexpr int CROW = D / 2;     // code bytes per Q/K row
@@ -194,6 +205,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   static_assert(KI % kWaves == 0 || kWaves % KI == 0, "fills split evenly over the waves");
   static_assert(VI % kWaves == 0 || kWaves % VI == 0, "fills split evenly over the waves");
   constexpr int KU = (KI + kWaves - 1) / kWaves, VU = (VI + kWaves - 1) / kWaves;  // fills per wave
+  static_assert(QBF16 || !VARLEN, "varlen batches take bf16 Q");
   __shared__ TileLds lds0, lds1;
 
   // Tile order: workgroup w is dispatched to XCD w % 8.  Each XCD gets a
@@ -202,16 +214,44 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   const int w = blockIdx.x;
   const int lin = (w & 7) * a.per_xcd + (w >> 3);
   if (lin >= a.BH * a.ntq) return;
-  const int64_t bh = lin / a.ntq;
-  const int qt = lin % a.ntq;
-  const int64_t hb = bh / a.H, hh = bh % a.H;
-  const int64_t qrow = hb * a.q_sb + hh * a.q_sh, orow0 = hb * a.o_sb + hh * a.o_sh;
+  const int64_t bh = lin / a.ntq;  // dense: batch * H + head; varlen: head
+  int qt = lin % a.ntq;
+  int N = a.N;
+  int64_t qrow, orow0;
+  int64_t krow0 = bh * int64_t(N);         // K code rows before this sequence
+  int vcs = a.vcs;                          // V channel stride in blocks
+  int64_t vblk0 = bh * int64_t(D) * vcs;    // V blocks before this head
+  int vskip = 0;                            // V blocks of this head before this sequence
+  if constexpr (VARLEN) {
+    // query tile qt of the varlen batch -> (sequence s, tile within s); the
+    // query-tile count is an upper bound, so trailing workgroups exit
+    const int n = a.batch + 1;
+    const int* row = a.vl;
+    const int* qtile = a.vl + n;
+    if (qt >= qtile[a.batch]) return;
+    const int s = find_segment(qtile, a.batch, qt);
+    const int tok0 = row[s];
+    N = row[s + 1] - tok0;
+    qt -= qtile[s];
+    qrow = tok0 * a.q_sn + bh * a.q_sh;
+    orow0 = tok0 * a.o_sn + bh * a.o_sh;
+    krow0 = bh * int64_t(a.kts) + tok0;
+    // V rows hold exactly the blocks of all sequences, blk[batch] per
+    // channel, so every block a tile reads past its sequence's last one is
+    // data the quantizer wrote (the next sequence's, or the next channel's)
+    vcs = a.vl[3 * n + a.batch];
+    vskip = a.vl[3 * n + s];
+    vblk0 = bh * int64_t(D) * vcs + vskip;
+  } else {
+    const int64_t hb = bh / a.H, hh = bh % a.H;
+    qrow = hb * a.q_sb + hh * a.q_sh;
+    orow0 = hb * a.o_sb + hh * a.o_sh;
+  }
 
   // wave index through readfirstlane: the compiler then keeps everything
   // derived from it (LDS fill destinations) in scalar registers
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g4 = lane >> 4;
-  const int N = a.N, nbn = a.nbn;
   const float c = a.c;
 
   // Q^T operand slices: query r16 of group g, d-block g4.  With bf16 Q the
@@ -256,15 +296,16 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   // Per-lane LDS offsets.  Sub-tile t of the K operand is k_lane + 256 t (the
   // swizzle term does not depend on t); channel tile ct of the V operand is
   // v_lane + 1024 ct; this lane's 8 scale bytes sit at s_lane.
-  const int k_lane = (32 * (r16 >> 2) + (r16 & 3)) * 64 + 16 * (g4 ^ (r16 >> 2) ^ (r16 & 2));
-  const int v_lane = r16 * 64 + 16 * (g4 ^ (r16 >> 2) ^ (r16 & 2));
+  const int k_row0 = 32 * (r16 >> 2) + (r16 & 3);
+  const int k_lane = k_row0 * 64 + 16 * (g4 ^ k_swz(k_row0));
+  const int v_lane = r16 * 64 + 16 * (g4 ^ v_swz(r16));
   const int s_lane = lane * 8;
 
   const int ntk = (N + kBC - 1) / kBC;
-  const uint8_t* kc_h = wave_uniform(a.kc + bh * int64_t(N) * CROW);
-  const uint8_t* ks_h = wave_uniform(a.ks + bh * int64_t(N) * DB);
-  const uint8_t* vc_h = wave_uniform(a.vc + bh * int64_t(D) * nbn * 16);
-  const uint8_t* vs_h = wave_uniform(a.vs + bh * int64_t(D) * nbn);
+  const uint8_t* kc_h = wave_uniform(a.kc + krow0 * CROW);
+  const uint8_t* ks_h = wave_uniform(a.ks + krow0 * DB);
+  const uint8_t* vc_h = wave_uniform(a.vc + vblk0 * 16);
+  const uint8_t* vs_h = wave_uniform(a.vs + vblk0);
 
   // Tile fetch.  Code chunks go straight from global memory into LDS (lane i
   // of a wave writes the 16 bytes at dst + 16 i), so the swizzle is applied on
@@ -282,7 +323,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   for (int u = 0; u < VU; ++u) {
     const int slot = (wave + u * kWaves) * 64 + lane;
     const int row = slot >> 2;
-    voff[u] = (row * nbn + ((slot & 3) ^ v_swz(row))) * 16;
+    voff[u] = (row * vcs + ((slot & 3) ^ v_swz(row))) * 16;
   }
   // Scale staging.  Thread tid < kBC carries the DB scale bytes of key kb + tid
   // (one load); the 4 D V scale bytes of the tile (item it: channel it % D,
@@ -303,7 +344,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   for (int v = 0; v < VB; ++v) {
     const int it = tid + NT * v, vch = it % D, vblk = it / D;
     vdst[v] = 64 * 8 + (vch & 15) * 8 + (vch >> 4) + 128 * vblk;
-    vso[v] = it < 4 * D ? uint32_t(vch * nbn + vblk) : 0x7FFFFFF0u;
+    vso[v] = it < 4 * D ? uint32_t(vch * vcs + vblk) : 0x7FFFFFF0u;
     vreg[v] = 0;
   }
   uint32_t kreg = 0;
@@ -312,10 +353,12 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   // first byte and whose record count is the bytes left in the head, so the
   // hardware range check returns zeros past the end.  K rows past N are zero
   // (and masked).  V code blocks and V scale bytes past the padded end of a
-  // channel read the next channel's finite data, which meets only zero
-  // weights.
-  const int khead = __builtin_amdgcn_readfirstlane(N * CROW), vhead = __builtin_amdgcn_readfirstlane(D * nbn * 16);
-  const int kshead = __builtin_amdgcn_readfirstlane(N * DB), vshead = __builtin_amdgcn_readfirstlane(D * nbn);
+  // channel (or, in a varlen batch, of a sequence) read the next channel's
+  // or sequence's finite data, which meets only zero weights.
+  const int khead = __builtin_amdgcn_readfirstlane(N * CROW);
+  const int vhead = __builtin_amdgcn_readfirstlane((D * vcs - vskip) * 16);
+  const int kshead = __builtin_amdgcn_readfirstlane(N * DB);
+  const int vshead = __builtin_amdgcn_readfirstlane(D * vcs - vskip);
   auto issue_tile = [&](int j, TileLds& T) {
     const int kb = j * kBC;
     const int vb0 = kb / 32;
@@ -471,11 +514,49 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   }
 }
 
+namespace {
+
+template <int D, int MODE, bool PNQ>
+void launch_variant(const AttnArgs& a, dim3 grid, bool qbf16, bool varlen, hipStream_t stream) {
+  const dim3 block(kWaves * 64);
+  if (varlen) attn_fwd_kernel<D, MODE, PNQ, true, true><<<grid, block, 0, stream>>>(a);
+  else if (qbf16) attn_fwd_kernel<D, MODE, PNQ, true, false><<<grid, block, 0, stream>>>(a);
+  else attn_fwd_kernel<D, MODE, PNQ, false, false><<<grid, block, 0, stream>>>(a);
+}
+
+hipError_t launch(AttnArgs& a, int d, int mode, bool pnq, bool varlen, float softmax_scale, hipStream_t stream) {
+  const int total = a.BH * a.ntq;
+  a.per_xcd = (total + 7) / 8;
+  a.c = softmax_scale * 1.4426950408889634f;
+  const dim3 grid(unsigned(a.per_xcd * 8));
+  const bool qbf16 = a.q != nullptr;
+  if (d == 128) {
+    if (mode == kModeUOS) {
+      if (pnq) launch_variant<128, kModeUOS, true>(a, grid, qbf16, varlen, stream);
+      else launch_variant<128, kModeUOS, false>(a, grid, qbf16, varlen, stream);
+    } else {
+      if (pnq) launch_variant<128, kModeOCP, true>(a, grid, qbf16, varlen, stream);
+      else launch_variant<128, kModeOCP, false>(a, grid, qbf16, varlen, stream);
+    }
+  } else {
+    if (mode == kModeUOS) {
+      if (pnq) launch_variant<64, kModeUOS, true>(a, grid, qbf16, varlen, stream);
+      else launch_variant<64, kModeUOS, false>(a, grid, qbf16, varlen, stream);
+    } else {
+      if (pnq) launch_variant<64, kModeOCP, true>(a, grid, qbf16, varlen, stream);
+      else launch_variant<64, kModeOCP, false>(a, grid, qbf16, varlen, stream);
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_attention(const uint16_t* q, const int64_t* q_strides, const uint8_t* qc, const uint8_t* qs,
                             const uint8_t* kc, const uint8_t* ks, const uint8_t* vc, const uint8_t* vs, int H,
                             int BH, int N, int d, int mode, bool pnq, float softmax_scale, uint16_t* o,
                             const int64_t* o_strides, hipStream_t stream) {
-  AttnArgs a;
+  AttnArgs a{};
   a.q = q; a.qc = qc; a.qs = qs; a.kc = kc; a.ks = ks; a.vc = vc; a.vs = vs; a.o = o;
   // null strides: dense [B][H][N][d]
   const int64_t dense[3] = {int64_t(H) * N * d, int64_t(N) * d, d};
@@ -486,26 +567,30 @@ hipError_t launch_attention(const uint16_t* q, const int64_t* q_strides, const u
   a.H = H;
   a.BH = BH;
   a.N = N;
-  a.nbn = (N + 31) / 32;
+  a.vcs = (N + 31) / 32;
   a.ntq = (N + kBR - 1) / kBR;
-  const int total = BH * a.ntq;
-  a.per_xcd = (total + 7) / 8;
-  a.c = softmax_scale * 1.4426950408889634f;
-  const dim3 grid(unsigned(a.per_xcd * 8)), block(kWaves * 64);
-#define MXATTN_LAUNCH(D_, M_, P_)                                          \
-  do {                                                                      \
-    if (q) attn_fwd_kernel<D_, M_, P_, true><<<grid, block, 0, stream>>>(a);  \
-    else attn_fwd_kernel<D_, M_, P_, false><<<grid, block, 0, stream>>>(a);   \
-  } while (0)
-  if (d == 128) {
-    if (mode == kModeUOS) { if (pnq) MXATTN_LAUNCH(128, kModeUOS, true); else MXATTN_LAUNCH(128, kModeUOS, false); }
-    else { if (pnq) MXATTN_LAUNCH(128, kModeOCP, true); else MXATTN_LAUNCH(128, kModeOCP, false); }
-  } else {
-    if (mode == kModeUOS) { if (pnq) MXATTN_LAUNCH(64, kModeUOS, true); else MXATTN_LAUNCH(64, kModeUOS, false); }
-    else { if (pnq) MXATTN_LAUNCH(64, kModeOCP, true); else MXATTN_LAUNCH(64, kModeOCP, false); }
-  }
-#undef MXATTN_LAUNCH
-  return hipGetLastError();
+  return launch(a, d, mode, pnq, false, softmax_scale, stream);
+}
+
+// Varlen batch: bf16 Q and O with token stride q_sn / o_sn and head stride
+// q_sh / o_sh (elements); K codes [H][T][d/2] (+ scales [H][T][d/32]); V codes
+// [H][d][B * 16] (+ scales [H][d][B]) with B = tab.blk[batch], the blocks of
+// all sequences, and sequence s in blocks tab.blk[s] ..; tab the varlen table
+// of `batch` sequences over T tokens.
+hipError_t launch_attention_varlen(const uint16_t* q, int64_t q_sn, int64_t q_sh, const uint8_t* kc,
+                                   const uint8_t* ks, const uint8_t* vc, const uint8_t* vs, const int* tab,
+                                   int batch, int T, int H, int d, int mode, bool pnq, float softmax_scale,
+                                   uint16_t* o, int64_t o_sn, int64_t o_sh, hipStream_t stream) {
+  AttnArgs a{};
+  a.q = q; a.kc = kc; a.ks = ks; a.vc = vc; a.vs = vs; a.o = o;
+  a.q_sn = q_sn; a.q_sh = q_sh; a.o_sn = o_sn; a.o_sh = o_sh;
+  a.H = H;
+  a.BH = H;
+  a.ntq = (T + kBR - 1) / kBR + batch;  // at least the query tiles of all sequences
+  a.vl = tab;
+  a.batch = batch;
+  a.kts = T;
+  return launch(a, d, mode, pnq, true, softmax_scale, stream);
 }
 
 }  // namespace mxattn

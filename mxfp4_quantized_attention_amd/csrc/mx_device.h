@@ -100,6 +100,19 @@ __device__ __forceinline__ uint32_t absmax8_bits(const uint4& v) {
 }
 
 
+// Largest s in [0, n) with pre[s] <= v, for a non-decreasing prefix array
+// pre of a varlen table (callers check v < pre[n] first, so the segment
+// found is never empty).
+__device__ __forceinline__ int find_segment(const int* pre, int n, int v) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pre[mid] <= v) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
 // One 16x16x128 MFMA on FP4 operands with E8M0 block scales.
 // A (16 rows x 128 K): lane l holds row l%16, K = 32*(l/16) + [0, 32) as 32
 // nibbles in a[0..3] (nibble n of the 128 bits = K offset n).  B (128 K x 16

@@ -135,6 +135,19 @@ __global__ __launch_bounds__(256) void quant_rows_strided_kernel(const uint16_t*
   }
 }
 
+// Rows of a varlen input split into segments (sequences): segment s covers
+// rows [row[s], row[s + 1]).  Its 256-row tiles are work tiles tile[s] ..
+// tile[s + 1] - 1, and its 32-row blocks are output blocks blk[s] ..
+// blk[s + 1] - 1 of every column, so blocks never straddle two segments and
+// the last block of each segment is zero-padded.  All three arrays hold
+// n + 1 prefix values (the varlen table, built on the device).
+struct RowSegments {
+  const int* row;
+  const int* tile;
+  const int* blk;
+  int n;
+};
+
 // Blocks along rows (axis 0).  Work item = a 256-row x 64-column bf16 tile
 // of one batch entry; each workgroup walks items with a grid stride and
 // holds the next item's loads in registers while it encodes the current one
@@ -143,36 +156,70 @@ __global__ __launch_bounds__(256) void quant_rows_strided_kernel(const uint16_t*
 // of eight 32-row blocks hit eight different banks; eight consecutive lanes
 // take the eight blocks of one column, so a wave writes whole 128-byte code
 // lines.  Rows past the end are zero (padding).
-template <int MODE>
+//
+// SEG: the rows are the segments of `seg`; ntr is then the number of work
+// tiles per entry (an upper bound on seg.tile[n]: items past it do nothing)
+// and every column holds exactly the blocks of all segments, seg.blk[n]
+// (vstride is ignored).  Otherwise ntr = ceil(rows / 256) and vstride = nb.
+template <int MODE, bool SEG>
 __global__ __launch_bounds__(256) void quant_cols_kernel(const uint16_t* __restrict__ x,
                                                          uint8_t* __restrict__ codes,
                                                          uint8_t* __restrict__ scales, int64_t rows,
-                                                         int64_t cols, int64_t nb, int64_t ntc, int64_t nitems,
-                                                         Layout3 in) {
+                                                         int64_t cols, int64_t ntr, int64_t ntc,
+                                                         int64_t nitems, int64_t vstride, Layout3 in,
+                                                         RowSegments seg) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[256 * 64];
   const int tid = threadIdx.x;
-  const int ntr = int((rows + 255) / 256);
   const bool vec8 = (cols & 7) == 0 && (in.sn & 7) == 0;
+  if constexpr (SEG) vstride = seg.blk[seg.n];
+  // One work item: entry bi, rows [r0, r0 + nrow) of the input (nrow <= 256),
+  // columns [c0, c0 + 64), output blocks blk0 .. blk0 + nblk - 1.
+  struct Item {
+    int64_t bi, r0, c0, blk0;
+    int nrow, nblk;
+  };
+  auto decode = [&](int64_t item) {
+    Item w;
+    w.bi = item / (ntr * ntc);
+    const int64_t rest = item % (ntr * ntc), tr = rest / ntc;
+    w.c0 = (rest % ntc) * 64;
+    if constexpr (SEG) {
+      w.nrow = 0;
+      w.nblk = 0;
+      w.r0 = w.blk0 = 0;
+      if (tr < seg.tile[seg.n]) {
+        const int s = find_segment(seg.tile, seg.n, int(tr));
+        const int lt = int(tr) - seg.tile[s];
+        const int len = seg.row[s + 1] - seg.row[s];
+        w.r0 = seg.row[s] + int64_t(lt) * 256;
+        w.nrow = min(256, len - lt * 256);
+        w.blk0 = seg.blk[s] + int64_t(lt) * 8;
+        w.nblk = (w.nrow + 31) / 32;
+      }
+    } else {
+      w.r0 = tr * 256;
+      w.nrow = int(min(int64_t(256), rows - w.r0));
+      w.blk0 = tr * 8;
+      w.nblk = (w.nrow + 31) / 32;
+    }
+    return w;
+  };
   v4u buf[8];
-  auto load = [&](int64_t item) {
-    const int64_t bi = item / (int64_t(ntr) * ntc), rest = item % (int64_t(ntr) * ntc);
-    const int64_t r0 = (rest / ntc) * 256, c0 = (rest % ntc) * 64;
-    const uint16_t* xb = x + in.base(bi);
+  auto load = [&](const Item& w) {
+    const uint16_t* xb = x + in.base(w.bi);
     const int cc = (tid & 7) * 8;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int rr = (tid >> 3) + 32 * i;
       buf[i] = v4u{0, 0, 0, 0};
-      if (r0 + rr < rows && c0 + cc < cols)
-        buf[i] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(xb + (r0 + rr) * in.sn + c0 + cc));
+      if (rr < w.nrow && w.c0 + cc < cols)
+        buf[i] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(xb + (w.r0 + rr) * in.sn + w.c0 + cc));
     }
   };
   int64_t item = blockIdx.x;
-  if (vec8 && item < nitems) load(item);
+  if (vec8 && item < nitems) load(decode(item));
   for (; item < nitems; item += gridDim.x) {
-    const int64_t bi = item / (int64_t(ntr) * ntc), rest = item % (int64_t(ntr) * ntc);
-    const int64_t tr = rest / ntc, tc = rest % ntc;
-    const int64_t r0 = tr * 256, c0 = tc * 64;
+    const Item w = decode(item);
     if (vec8) {
       const int cc = (tid & 7) * 8;
 #pragma unroll
@@ -181,21 +228,20 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const uint16_t* __restr
         *reinterpret_cast<v4u*>(&tile[rr * 64 + (cc ^ (8 * i))]) = buf[i];
       }
     } else {
-      const uint16_t* xb = x + in.base(bi);
+      const uint16_t* xb = x + in.base(w.bi);
       for (int i = tid; i < 256 * 64; i += 256) {
         const int rr = i >> 6, cc = i & 63;
         tile[rr * 64 + (cc ^ (8 * (rr >> 5)))] =
-            (r0 + rr < rows && c0 + cc < cols) ? xb[(r0 + rr) * in.sn + c0 + cc] : uint16_t(0);
+            (rr < w.nrow && w.c0 + cc < cols) ? xb[(w.r0 + rr) * in.sn + w.c0 + cc] : uint16_t(0);
       }
     }
     __syncthreads();
-    if (vec8 && item + gridDim.x < nitems) load(item + gridDim.x);
+    if (vec8 && item + gridDim.x < nitems) load(decode(item + gridDim.x));
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int it = tid + 256 * k;
       const int jb = it & 7, c = it >> 3;
-      const int64_t blk = tr * 8 + jb;
-      if (c0 + c >= cols || blk >= nb) continue;
+      if (w.c0 + c >= cols || jb >= w.nblk) continue;
       float f[32];
       uint32_t m = 0;
 #pragma unroll
@@ -210,11 +256,92 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const uint16_t* __restr
       cw.y = encode8(f[8], f[9], f[10], f[11], f[12], f[13], f[14], f[15], e);
       cw.z = encode8(f[16], f[17], f[18], f[19], f[20], f[21], f[22], f[23], e);
       cw.w = encode8(f[24], f[25], f[26], f[27], f[28], f[29], f[30], f[31], e);
-      const int64_t vec = bi * cols + c0 + c;
-      __builtin_nontemporal_store(cw, reinterpret_cast<v4u*>(codes + (vec * nb + blk) * 16));
-      scales[vec * nb + blk] = uint8_t(e + 127);
+      const int64_t out = (w.bi * cols + w.c0 + c) * vstride + w.blk0 + jb;
+      __builtin_nontemporal_store(cw, reinterpret_cast<v4u*>(codes + out * 16));
+      scales[out] = uint8_t(e + 127);
     }
     __syncthreads();
+  }
+}
+
+// The varlen table from cu_seqlens (batch + 1 entries, device memory): four
+// arrays of batch + 1 ints, one after the other,
+//   row[s]   = start token of sequence s: cu_seqlens clamped to [0, T] and
+//              made non-decreasing (running maximum), so every sequence is a
+//              token range inside [0, T) whatever the input holds;
+//   qtile[s] = sum over earlier sequences of ceil(len / 128)  (attention
+//              query tiles);
+//   vtile[s] = sum of ceil(len / 256)  (row tiles of the V quantizer);
+//   blk[s]   = sum of ceil(len / 32)   (32-token V blocks).
+// One workgroup; each thread takes a contiguous chunk of entries, and the
+// chunk totals are scanned in LDS.
+__global__ __launch_bounds__(256) void varlen_table_kernel(const int* __restrict__ cu, int batch, int T,
+                                                           int* __restrict__ tab) {
+  __shared__ int part[4][256];
+  const int n = batch + 1, tid = threadIdx.x;
+  const int per = (n + 255) / 256;
+  const int i0 = min(n, tid * per), i1 = min(n, i0 + per);
+  int* row = tab;
+  int* qtile = tab + n;
+  int* vtile = tab + 2 * n;
+  int* blk = tab + 3 * n;
+  int m = 0;
+  for (int i = i0; i < i1; ++i) m = max(m, min(max(cu[i], 0), T));
+  part[0][tid] = m;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int t = 0; t < 256; ++t) {
+      const int v = part[0][t];
+      part[0][t] = run;
+      run = max(run, v);
+    }
+  }
+  __syncthreads();
+  m = part[0][tid];
+  for (int i = i0; i < i1; ++i) {
+    m = max(m, min(max(cu[i], 0), T));
+    row[i] = m;
+  }
+  __threadfence_block();
+  __syncthreads();
+  int sq = 0, sv = 0, sb = 0;
+  for (int i = i0; i < i1 && i < batch; ++i) {
+    const int len = row[i + 1] - row[i];
+    sq += (len + 127) / 128;
+    sv += (len + 255) / 256;
+    sb += (len + 31) / 32;
+  }
+  part[1][tid] = sq;
+  part[2][tid] = sv;
+  part[3][tid] = sb;
+  __syncthreads();
+  if (tid == 0) {
+    int rq = 0, rv = 0, rb = 0;
+    for (int t = 0; t < 256; ++t) {
+      const int a = part[1][t], b = part[2][t], c = part[3][t];
+      part[1][t] = rq;
+      part[2][t] = rv;
+      part[3][t] = rb;
+      rq += a;
+      rv += b;
+      rb += c;
+    }
+  }
+  __syncthreads();
+  sq = part[1][tid];
+  sv = part[2][tid];
+  sb = part[3][tid];
+  for (int i = i0; i < i1; ++i) {
+    qtile[i] = sq;
+    vtile[i] = sv;
+    blk[i] = sb;
+    if (i < batch) {
+      const int len = row[i + 1] - row[i];
+      sq += (len + 127) / 128;
+      sv += (len + 255) / 256;
+      sb += (len + 31) / 32;
+    }
   }
 }
 
@@ -256,12 +383,13 @@ hipError_t launch_quantize(const void* x, int64_t batch, int64_t rows, int64_t c
     const int64_t nitems = batch * ntr * ntc;
     const int64_t grid = nitems < kColsGrid ? nitems : kColsGrid;
     const Layout3 dense{1, rows * cols, 0, cols};
+    const RowSegments none{nullptr, nullptr, nullptr, 0};
     if (mode == kModeUOS)
-      quant_cols_kernel<kModeUOS><<<dim3(unsigned(grid)), dim3(256), 0, stream>>>(static_cast<const uint16_t*>(x),
-                                                                   codes, scales, rows, cols, nb, ntc, nitems, dense);
+      quant_cols_kernel<kModeUOS, false><<<dim3(unsigned(grid)), dim3(256), 0, stream>>>(
+          static_cast<const uint16_t*>(x), codes, scales, rows, cols, ntr, ntc, nitems, nb, dense, none);
     else
-      quant_cols_kernel<kModeOCP><<<dim3(unsigned(grid)), dim3(256), 0, stream>>>(static_cast<const uint16_t*>(x),
-                                                                   codes, scales, rows, cols, nb, ntc, nitems, dense);
+      quant_cols_kernel<kModeOCP, false><<<dim3(unsigned(grid)), dim3(256), 0, stream>>>(
+          static_cast<const uint16_t*>(x), codes, scales, rows, cols, ntr, ntc, nitems, nb, dense, none);
   }
   return hipGetLastError();
 }
@@ -294,13 +422,45 @@ hipError_t launch_quantize_strided(const void* x, int64_t B, int64_t H, int64_t 
     const int64_t ntr = (rows + 255) / 256, ntc = (cols + 63) / 64;
     const int64_t nitems = B * H * ntr * ntc;
     const int64_t grid = nitems < kColsGrid ? nitems : kColsGrid;
+    const RowSegments none{nullptr, nullptr, nullptr, 0};
     if (mode == kModeUOS)
-      quant_cols_kernel<kModeUOS><<<dim3(unsigned(grid)), dim3(256), 0, stream>>>(xp, codes, scales, rows, cols, nb,
-                                                                                   ntc, nitems, in);
+      quant_cols_kernel<kModeUOS, false><<<dim3(unsigned(grid)), dim3(256), 0, stream>>>(
+          xp, codes, scales, rows, cols, ntr, ntc, nitems, nb, in, none);
     else
-      quant_cols_kernel<kModeOCP><<<dim3(unsigned(grid)), dim3(256), 0, stream>>>(xp, codes, scales, rows, cols, nb,
-                                                                                   ntc, nitems, in);
+      quant_cols_kernel<kModeOCP, false><<<dim3(unsigned(grid)), dim3(256), 0, stream>>>(
+          xp, codes, scales, rows, cols, ntr, ntc, nitems, nb, in, none);
   }
+  return hipGetLastError();
+}
+
+// Varlen table (see varlen_table_kernel) into tab[4 (batch + 1)].
+hipError_t launch_varlen_table(const int* cu_seqlens, int batch, int T, int* tab, hipStream_t stream) {
+  varlen_table_kernel<<<dim3(1), dim3(256), 0, stream>>>(cu_seqlens, batch, T, tab);
+  return hipGetLastError();
+}
+
+// V of a varlen batch, [T][H][d] with element (t, h, c) at x + t sn + h sh + c,
+// quantized along tokens per sequence: codes [H][d][B * 16] and scales
+// [H][d][B] with B = blk[batch] (at most ceil(T / 32) + batch), sequence s
+// in blocks blk[s] .. blk[s + 1] - 1 of every channel.  tab is the varlen
+// table.
+hipError_t launch_quantize_varlen_cols(const void* x, int batch, int64_t T, int64_t H, int64_t d, int64_t sh,
+                                       int64_t sn, const int* tab, int mode, uint8_t* codes, uint8_t* scales,
+                                       hipStream_t stream) {
+  if (T == 0 || H == 0) return hipSuccess;
+  const int n = batch + 1;
+  const RowSegments seg{tab, tab + 2 * n, tab + 3 * n, batch};
+  const Layout3 in{H, 0, sh, sn};
+  const int64_t ntr = (T + 255) / 256 + batch, ntc = (d + 63) / 64;
+  const int64_t nitems = H * ntr * ntc;
+  const int64_t grid = nitems < kColsGrid ? nitems : kColsGrid;
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+  if (mode == kModeUOS)
+    quant_cols_kernel<kModeUOS, true><<<dim3(unsigned(grid)), dim3(256), 0, stream>>>(
+        xp, codes, scales, T, d, ntr, ntc, nitems, 0, in, seg);
+  else
+    quant_cols_kernel<kModeOCP, true><<<dim3(unsigned(grid)), dim3(256), 0, stream>>>(
+        xp, codes, scales, T, d, ntr, ntc, nitems, 0, in, seg);
   return hipGetLastError();
 }
 

@@ -228,6 +228,47 @@ def attn_rows(q, k, v, BH: int, N: int, d: int, mode: int, pnq: bool, Bc: int,
     return res
 
 
+def attn_varlen_rows(q, k, v, cu_seqlens, H: int, d: int, mode: int, pnq: bool, Bc: int,
+                     softmax_scale: float, rows, want_budget: bool = True):
+    """Oracle attention over a varlen batch: q, k, v are bf16 bit patterns
+    [T][H][d] (tokens packed along one axis) and sequence s holds tokens
+    [cu_seqlens[s], cu_seqlens[s+1]).  Every sequence is its own attention
+    problem: a query attends to the keys of its own sequence only, with key
+    tiles and 32-key blocks counted from the sequence's first token, which is
+    ``attn_rows`` on that sequence's slice.  ``rows`` are (token, head)
+    pairs [nrows][2]; each token must lie in some sequence.  Returns the
+    ``attn_rows`` dict fields for the rows in the order given."""
+    q = _c(q, np.uint16)
+    k = _c(k, np.uint16)
+    v = _c(v, np.uint16)
+    T = q.size // (H * d)
+    q, k, v = (a.reshape(T, H, d) for a in (q, k, v))
+    cu = np.asarray(cu_seqlens, np.int64)
+    rows = np.asarray(rows, np.int64).reshape(-1, 2)
+    nr = rows.shape[0]
+    out = np.empty((nr, d), np.float64)
+    lsum = np.empty(nr, np.float64)
+    tie = np.zeros(nr, bool)
+    budget = np.zeros((nr, d), np.float64)
+    seq = np.searchsorted(cu, rows[:, 0], side="right") - 1
+    for s in np.unique(seq):
+        t0, t1 = int(cu[s]), int(cu[s + 1])
+        assert 0 <= s < cu.size - 1 and t0 < t1
+        for h in np.unique(rows[seq == s, 1]):
+            sel = np.nonzero((seq == s) & (rows[:, 1] == h))[0]
+            part = attn_rows(q[t0:t1, h], k[t0:t1, h], v[t0:t1, h], 1, t1 - t0, d, mode, pnq, Bc,
+                             softmax_scale, rows[sel, 0] - t0, want_budget=want_budget)
+            out[sel] = part["out"]
+            lsum[sel] = part["l"]
+            tie[sel] = part["near_tie"]
+            if want_budget:
+                budget[sel] = part["budget"]
+    res = {"out": out, "out_bf16": f64_to_bf16(out), "l": lsum, "near_tie": tie}
+    if want_budget:
+        res["budget"] = budget
+    return res
+
+
 def gemm_rows(x, w, M: int, N: int, K: int, mode: int, rows=None):
     """Oracle MXFP4 GEMM: Y = X_q W_q^T for the rows ``rows`` of X (all rows if
     None).  x: bf16 bits [M][K], w: bf16 bits [N][K]; both are quantized

@@ -125,6 +125,44 @@ def test_strided_argument_errors():
     assert q(None, 0, 1, 64, 128, s3(0, 0, 128), 1, 1, None, None, None) == OK   # empty: no-op
 
 
+def test_varlen_workspace_and_argument_errors():
+    import ctypes
+    L = mx.lib()
+    A = 1 << 20
+    T, H, d, batch = 1000, 4, 128, 3
+    w = mx.varlen_workspace_bytes(batch, T, H, d)
+    vstride = (T + 31) // 32 + batch
+    need = H * T * d // 2 + H * T * 4 + H * d * vstride * 17 + 4 * (batch + 1) * 4
+    assert need <= w < need + 5 * 256
+    assert mx.varlen_workspace_bytes(0, T, H, d) == 0
+    assert mx.varlen_workspace_bytes(batch, T, H, 96) == 0
+    assert mx.varlen_workspace_bytes(batch, -1, H, d) == 0
+    s8 = lambda *v: (ctypes.c_int64 * 8)(*v)
+
+    def fwd(q=A, o=A, cu=A, batch=batch, T=T, H=H, d=d, st=None, mode=1, pnq=1, scale=0.0, ws=A, wsb=1 << 40):
+        return L.mxattn_fwd_varlen(q, A, A, o, cu, batch, T, H, d, st, mode, pnq, scale, ws, wsb, None)
+
+    assert fwd(batch=0) == INVALID
+    assert fwd(H=0) == INVALID
+    assert fwd(T=-1) == INVALID
+    assert fwd(T=0) == OK                      # nothing to do, nothing launched
+    assert fwd(d=96) == UNSUPPORTED
+    assert fwd(H=70000) == UNSUPPORTED
+    assert fwd(T=(1 << 24) + 1) == UNSUPPORTED
+    assert fwd(batch=(1 << 20) + 1) == UNSUPPORTED
+    assert fwd(cu=None) == INVALID
+    assert fwd(cu=A + 2) == INVALID            # cu_seqlens must be 4-byte aligned
+    assert fwd(q=A + 2) == INVALID
+    assert fwd(mode=5) == INVALID
+    assert fwd(pnq=3) == INVALID
+    assert fwd(scale=float("nan")) == INVALID
+    assert fwd(st=s8(512, 128, 512, 128, 512, 128, 512, 12)) == INVALID  # not a multiple of 8
+    assert fwd(st=s8(512, 128, -512, 128, 512, 128, 512, 128)) == INVALID
+    assert fwd(ws=None) == WORKSPACE
+    assert fwd(wsb=w - 1) == WORKSPACE
+    assert fwd(ws=A + 8) == INVALID
+
+
 def test_dump_from_host_memory(tmp_path):
     import oracle
     import workloads

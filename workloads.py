@@ -22,6 +22,10 @@ weights, prompts or videos from those models are used or needed):
   gemm     X [32760][5120] (Wan-style tokens x hidden: Student-t(4) times a
            LogNormal(0, 1) scale per channel), W [13824][5120] (an FFN
            up-projection) ~ N(0, 0.02^2); both bf16
+  wan_varlen a varlen batch of four Wan-style videos of 21, 13, 5 and 1
+           latent frames (1560 tokens each: N = 32760, 20280, 7800, 1560,
+           T = 62400 packed tokens), H=40, d=128, the Wan value distribution
+           per (sequence, head)
   tie_case structured Q/K (and a chosen softmax scale) that put one
            exponential in eight on an E2M1 rounding tie; V ~ N(0, 1)
 
@@ -165,6 +169,31 @@ def tie_case(N: int = 256, d: int = 64, seed: int = 9):
     v = np.random.default_rng(seed).standard_normal((N, d)).astype(np.float32)
     scale = float(-2.0 * np.log(0.3125))
     return f32_to_bf16(q), f32_to_bf16(k), f32_to_bf16(v), scale
+
+
+VARLEN_CONFIGS = {
+    "wan_varlen": dict(lengths=(32760, 20280, 7800, 1560), H=40, d=128, seed=6, dist="wan"),
+}
+
+
+def varlen_qkv(lengths, H: int, d: int, seed: int, dist: str = "wan", threads: int | None = None):
+    """Q, K, V of a varlen batch as bf16 bit patterns packed [T][H][d], plus
+    cu_seqlens (int32, len(lengths) + 1).  Sequence s, head h draws like head
+    (b = s, h) of the named distribution at N = lengths[s]."""
+    lengths = [int(n) for n in lengths]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T = int(cu[-1])
+    out = {t: np.empty((T, H, d), np.uint16) for t in ("q", "k", "v")}
+    jobs = [(t, s, h) for t in ("q", "k", "v") for s in range(len(lengths)) for h in range(H) if lengths[s] > 0]
+
+    def fill(job):
+        t, s, h = job
+        out[t][cu[s]:cu[s + 1], h] = head(dist, t, s, h, seed=seed, N=lengths[s], d=d)
+
+    nt = threads or min(16, os.cpu_count() or 1)
+    with ThreadPoolExecutor(max_workers=nt) as ex:
+        list(ex.map(fill, jobs))
+    return out["q"], out["k"], out["v"], cu
 
 
 GEMM_CONFIGS = {
