@@ -23,6 +23,14 @@ packed tokens, H=40, d=128, UOS + PNQ); one step = one mxattn_fwd_varlen
 call (varlen table, K and V quantization, the fused kernel), and the FLOP
 count is 4*H*d*sum(N_s^2).
 
+`--workload wan_block` times the attention block of a Wan-style DiT layer
+from its input activations: X [32760][5120] bf16 and W_qkv [15360][5120]
+(quantized once beforehand); one step = quantize X, the QKV projection with
+the epilogue that writes bf16 Q and MXFP4 K and V in the attention layouts
+(mxqkv_proj), and the fused attention kernel.  The same work unfused (bf16
+Y from mxgemm, then mxattn_fwd_strided on its Q, K, V slices) is timed
+beside it.
+
 `--workload sweep` instead times the quantizer alone (mxq_quantize) over
 n = 2^p bf16 values, p = 20..30 (log-uniform magnitudes 2^-20..2^10, random
 sign, viewed [n/1024, 1024]), UOS and OCP along the contiguous axis, plus one
@@ -147,7 +155,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="wan", choices=["tiny", "small", "wan", "hunyuan", "sweep", "gemm", "wan_varlen"])
+    ap.add_argument("--workload", default="wan", choices=["tiny", "small", "wan", "hunyuan", "sweep", "gemm", "wan_varlen", "wan_block"])
     ap.add_argument("--mode", default="uos", choices=["uos", "ocp"])
     ap.add_argument("--no-pnq", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -179,6 +187,9 @@ def main():
         return
     if args.workload == "wan_varlen":
         varlen_bench(args, dev)
+        return
+    if args.workload == "wan_block":
+        block_bench(args, dev)
         return
     cfg = workloads.CONFIGS[args.workload]
     B, H, N, d = cfg["B"], cfg["H"], cfg["N"], cfg["d"]
@@ -521,6 +532,129 @@ def varlen_bench(args, dev):
             "max_diff_over_bound_unflagged_rows": float(over[~flagged].max()) if (~flagged).any() else 0.0,
             "flagged_rows": int(flagged.sum()),
         }
+    print(json.dumps(result), flush=True)
+
+
+def block_bench(args, dev):
+    """The Wan attention block from its input activations (see the module
+    docstring)."""
+    import numpy as np
+    import torch
+    import workloads
+    import mxfp4_quantized_attention_amd as mx
+
+    T, C, H, d = 32760, 5120, 40, 128
+    HD = H * d
+    mode = mx.MODE_UOS if args.mode == "uos" else mx.MODE_OCP
+    pnq = 0 if args.no_pnq else 1
+    log(f"[bench] wan_block: generating X [{T}][{C}], W_qkv [{3 * HD}][{C}]")
+    x, w = workloads.gemm_inputs(M=T, N=3 * HD, K=C, seed=7)
+    up = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    xg, wg = up(x), up(w)
+    del x, w
+    L = mx.lib()
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    u8 = dict(dtype=torch.uint8, device=dev)
+    wc, ws = torch.empty(3 * HD * C // 2, **u8), torch.empty(3 * HD * C // 32, **u8)
+    if L.mxq_quantize(wg.data_ptr(), 1, 3 * HD, C, 1, mode, wc.data_ptr(), ws.data_ptr(), sp) != 0:
+        raise RuntimeError("weight quantization failed")
+    xc, xs = torch.empty(T * C // 2, **u8), torch.empty(T * C // 32, **u8)
+    nbm = (T + 31) // 32
+    q = torch.empty((1, H, T, d), dtype=torch.bfloat16, device=dev)
+    kc, ks = torch.empty(H * T * d // 2, **u8), torch.empty(H * T * d // 32, **u8)
+    vc, vs = torch.empty(H * d * nbm * 16, **u8), torch.empty(H * d * nbm, **u8)
+    o = torch.empty_like(q)
+
+    def launch_x():
+        return L.mxq_quantize(xg.data_ptr(), 1, T, C, 1, mode, xc.data_ptr(), xs.data_ptr(), sp)
+
+    def launch_qkv():
+        return L.mxqkv_proj_quantized(xc.data_ptr(), xs.data_ptr(), wc.data_ptr(), ws.data_ptr(), T, C, H, d, mode,
+                                      q.data_ptr(), kc.data_ptr(), ks.data_ptr(), vc.data_ptr(), vs.data_ptr(), sp)
+
+    def launch_attn():
+        return L.mxattn_fwd_kv_quantized(q.data_ptr(), kc.data_ptr(), ks.data_ptr(), vc.data_ptr(), vs.data_ptr(),
+                                         1, H, T, d, mode, pnq, 0.0, o.data_ptr(), sp)
+
+    launches = (launch_x, launch_qkv, launch_attn)
+
+    def run(fns, steps, warmup):
+        def step(ev=None):
+            for i, fn in enumerate(fns):
+                if ev is not None:
+                    ev[i].record(stream)
+                st = fn()
+                if st != 0:
+                    raise RuntimeError(f"launch {i} failed: {mx.status_string(st)}")
+            if ev is not None:
+                ev[len(fns)].record(stream)
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(steps)]
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(events[i])
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        per = np.array([[ev[i].elapsed_time(ev[i + 1]) for i in range(len(fns))] for ev in events]).mean(axis=0)
+        return ms, per
+
+    log(f"[bench] fused block: warmup {args.warmup}, timing {args.steps} steps")
+    ms_per_step, per = run(launches, args.steps, args.warmup)
+    kx, kq, ka = per
+    flop_gemm = 2.0 * T * C * 3 * HD
+    flop_attn = 4.0 * H * T * T * d
+    flop = flop_gemm + flop_attn
+    value = flop / (ms_per_step * 1e-3) / 1e12
+    log(f"[bench] wan_block step {ms_per_step:.3f} ms -> {value:.1f} TFLOP/s; quantize X {kx:.3f} ms, "
+        f"QKV projection {kq:.3f} ms ({flop_gemm / (kq * 1e-3) / 1e12:.1f} TFLOP/s), attention {ka:.3f} ms")
+
+    # unfused: bf16 Y from the GEMM, then mxattn_fwd_strided on its slices
+    y = torch.empty((T, 3 * HD), dtype=torch.bfloat16, device=dev)
+    o2 = torch.empty((1, H, T, d), dtype=torch.bfloat16, device=dev)
+    wsb = mx.workspace_bytes(1, H, T, d)
+    wsp = torch.empty(wsb, **u8)
+    import ctypes
+    s_qkv = (ctypes.c_int64 * 3)(0, d, 3 * HD)
+    s_o = (ctypes.c_int64 * 3)(H * T * d, T * d, d)
+
+    def launch_y():
+        return L.mxgemm_quantized(xc.data_ptr(), xs.data_ptr(), wc.data_ptr(), ws.data_ptr(), T, 3 * HD, C,
+                                  y.data_ptr(), sp)
+
+    def launch_strided():
+        base = y.data_ptr()
+        return L.mxattn_fwd_strided(base, base + 2 * HD, base + 4 * HD, o2.data_ptr(), 1, H, T, d, s_qkv, s_qkv, s_qkv,
+                                    s_o, mode, pnq, 0.0, wsp.data_ptr(), wsb, sp)
+
+    log("[bench] unfused block")
+    ms_unfused, per_u = run((launch_x, launch_y, launch_strided), args.steps, args.warmup)
+    same = bool(torch.equal(o.view(torch.int16), o2.view(torch.int16)))
+    log(f"[bench] unfused step {ms_unfused:.3f} ms (GEMM to bf16 {per_u[1]:.3f} ms, K/V quantize + attention "
+        f"{per_u[2]:.3f} ms); outputs identical: {same}")
+    result = {
+        "metric": "MXFP4 attention block TFLOP/s (QKV projection 2*T*C*3*H*d + attention 4*H*T^2*d), "
+                  "and % of MI355X MXFP4 MFMA peak",
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "mxfp4", "data": "synthetic",
+        "config": {"workload": f"wan_block: X [{T}][{C}] bf16 -> QKV projection ({3 * HD} outputs, W quantized once) "
+                               f"-> attention H={H} N={T} d={d} non-causal, {args.mode.upper()}"
+                               f"{'+PNQ' if pnq else ''}", "T": T, "C": C, "H": H, "d": d, "mode": args.mode,
+                   "pnq": bool(pnq), "parallelism": "single GPU"},
+        "pct_of_fp4_peak": 100.0 * value / PEAK_FP4_TFLOPS,
+        "roofline": {"bound": "mfma", "achieved": flop_attn / (ka * 1e-3) / 1e12, "peak": PEAK_FP4_TFLOPS,
+                     "unit": "TFLOP/s", "frac": flop_attn / (ka * 1e-3) / 1e12 / PEAK_FP4_TFLOPS, "traffic": None,
+                     "kernel": "attn_fwd_kernel", "kernel_ms": ka,
+                     "algorithmic": f"4*d FLOP per score element x H*T^2 = {flop_attn:.4g} FLOP per launch"},
+        "qkv_projection": {"ms": kq, "tflops": flop_gemm / (kq * 1e-3) / 1e12,
+                           "frac": flop_gemm / (kq * 1e-3) / 1e12 / PEAK_FP4_TFLOPS},
+        "quantize_x_ms": kx,
+        "unfused_ms_per_step": ms_unfused,
+        "fused_equals_unfused": same,
+    }
     print(json.dumps(result), flush=True)
 
 

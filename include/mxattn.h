@@ -247,6 +247,42 @@ int mxgemm(const void *x, const uint8_t *wc, const uint8_t *ws, int64_t M, int64
            int mode, void *y, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * mxqkv_proj_quantized -- the QKV projection of one sequence of T tokens,
+ * Y = X W^T (as mxgemm_quantized, with N = 3*H*d), written straight into the
+ * operand formats of the attention kernel (the MXAttention abstract notes
+ * that quantization fused into the attention pipeline costs little): Y's
+ * columns are [Q | K | V], each H*d wide, head-major inside each part.
+ *   q:  bf16 [H][T][d]                       (Q, for mxattn_fwd_kv_quantized)
+ *   kc: [H][T][d/2],  ks: [H][T][d/32]       (K quantized along d)
+ *   vc: [H][d][ceil(T/32)*16], vs: [H][d][ceil(T/32)]   (V quantized along T)
+ * K and V are rounded to bf16 (nearest even) and then quantized with `mode`,
+ * exactly as mxq_quantize would quantize that bf16 K and V, so the codes and
+ * scales equal those of mxgemm_quantized followed by mxq_quantize of the K
+ * and V parts; the last V block of each channel is zero-padded.  These are
+ * the layouts mxattn_fwd_kv_quantized takes with B = 1, N = T.
+ * xc, xs, wc, ws: X [T][C] and W [3*H*d][C] quantized along C (canonical
+ * layout).  Requires C % 128 == 0, d in {64, 128}; code pointers and q 16-byte
+ * aligned, xs and ws 4-byte aligned; all pointers device memory owned by the
+ * caller.
+ * Errors: MXQ_ERR_INVALID_ARG (null or misaligned pointer, T/C/H < 1, mode),
+ * MXQ_ERR_UNSUPPORTED (d, C, or sizes past the GEMM's or the attention's
+ * limits), MXQ_ERR_HIP.
+ */
+int mxqkv_proj_quantized(const uint8_t *xc, const uint8_t *xs, const uint8_t *wc, const uint8_t *ws,
+                         int64_t T, int64_t C, int64_t H, int64_t d, int mode, void *q, uint8_t *kc,
+                         uint8_t *ks, uint8_t *vc, uint8_t *vs, void *stream);
+
+/*
+ * mxqkv_proj -- mxqkv_proj_quantized from bf16 X [T][C]: X is quantized with
+ * `mode` into the workspace first (mxgemm_workspace_bytes(T, C) bytes), W as
+ * for mxqkv_proj_quantized.  Errors as mxqkv_proj_quantized, plus
+ * MXQ_ERR_WORKSPACE.
+ */
+int mxqkv_proj(const void *x, const uint8_t *wc, const uint8_t *ws, int64_t T, int64_t C, int64_t H,
+               int64_t d, int mode, void *q, uint8_t *kc, uint8_t *ks, uint8_t *vc, uint8_t *vs,
+               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * mxq_dump -- write quantized data in the reference format "MXQ1": a 256-byte
  * header of ASCII JSON padded with spaces and ending in '\n'
  *   {"magic":"MXQ1","version":1,"mode":"ocp"|"uos","axis":A,"batch":B,

@@ -72,6 +72,10 @@ def lib() -> ctypes.CDLL:
     L.mxattn_varlen_workspace_bytes.restype = ctypes.c_size_t
     L.mxattn_fwd_varlen.argtypes = [P, P, P, P, P, i64, i64, i64, i64, P, i32, i32, f32, P, ctypes.c_size_t, P]
     L.mxattn_fwd_varlen.restype = i32
+    L.mxqkv_proj_quantized.argtypes = [P, P, P, P, i64, i64, i64, i64, i32, P, P, P, P, P, P]
+    L.mxqkv_proj_quantized.restype = i32
+    L.mxqkv_proj.argtypes = [P, P, P, i64, i64, i64, i64, i32, P, P, P, P, P, P, ctypes.c_size_t, P]
+    L.mxqkv_proj.restype = i32
     _lib = L
     return L
 
@@ -79,7 +83,8 @@ def lib() -> ctypes.CDLL:
 EXPORTS = ("mxq_status_string", "mxattn_version", "mxq_quantize", "mxattn_kv_tile",
            "mxattn_workspace_bytes", "mxattn_fwd", "mxattn_fwd_quantized", "mxattn_fwd_kv_quantized",
            "mxgemm_quantized", "mxgemm_workspace_bytes", "mxgemm", "mxattn_fwd_strided",
-           "mxq_quantize_strided", "mxq_dump", "mxattn_varlen_workspace_bytes", "mxattn_fwd_varlen")
+           "mxq_quantize_strided", "mxq_dump", "mxattn_varlen_workspace_bytes", "mxattn_fwd_varlen",
+           "mxqkv_proj_quantized", "mxqkv_proj")
 
 
 def status_string(status: int) -> str:
@@ -310,6 +315,41 @@ def gemm(x, wc, ws, N: int, mode="uos", out=None, workspace=None):
     _check(lib().mxgemm(x.data_ptr(), wc.data_ptr(), ws.data_ptr(), M, N, K, _mode(mode), y.data_ptr(),
                         workspace.data_ptr(), workspace.numel(), _stream(x)), "mxgemm")
     return y
+
+
+def _qkv_outputs(T, H, d, dev):
+    import torch
+    u8 = dict(dtype=torch.uint8, device=dev)
+    nbm = n_blocks(T)
+    q = torch.empty((1, H, T, d), dtype=torch.bfloat16, device=dev)
+    return (q, torch.empty(H * T * d // 2, **u8), torch.empty(H * T * d // 32, **u8),
+            torch.empty(H * d * nbm * 16, **u8), torch.empty(H * d * nbm, **u8))
+
+
+def qkv_proj_quantized(xc, xs, wc, ws, T: int, C: int, H: int, d: int, mode="uos"):
+    """mxqkv_proj_quantized: returns (q [1, H, T, d] bf16, kc, ks, vc, vs) in
+    the layouts fwd_kv_quantized takes with B = 1, N = T."""
+    q, kc, ks, vc, vs = _qkv_outputs(T, H, d, xc.device)
+    _check(lib().mxqkv_proj_quantized(xc.data_ptr(), xs.data_ptr(), wc.data_ptr(), ws.data_ptr(), T, C, H, d,
+                                      _mode(mode), q.data_ptr(), kc.data_ptr(), ks.data_ptr(), vc.data_ptr(),
+                                      vs.data_ptr(), _stream(xc)), "mxqkv_proj_quantized")
+    return q, kc, ks, vc, vs
+
+
+def qkv_proj(x, wc, ws, H: int, d: int, mode="uos", workspace=None):
+    """mxqkv_proj on bf16 x [T, C] (W quantized beforehand with quantize(...,
+    axis=1) as [3*H*d, C]); returns (q, kc, ks, vc, vs) as qkv_proj_quantized."""
+    import torch
+    x = _bf16_device(x, "x")
+    T, C = x.shape
+    q, kc, ks, vc, vs = _qkv_outputs(T, H, d, x.device)
+    need = int(lib().mxgemm_workspace_bytes(T, C))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _check(lib().mxqkv_proj(x.data_ptr(), wc.data_ptr(), ws.data_ptr(), T, C, H, d, _mode(mode), q.data_ptr(),
+                            kc.data_ptr(), ks.data_ptr(), vc.data_ptr(), vs.data_ptr(), workspace.data_ptr(),
+                            workspace.numel(), _stream(x)), "mxqkv_proj")
+    return q, kc, ks, vc, vs
 
 
 def dump(path: str, codes, scales, batch: int, nvec: int, L: int, axis: int, mode="uos") -> None:

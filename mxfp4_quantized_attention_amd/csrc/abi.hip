@@ -24,6 +24,9 @@ hipError_t launch_quantize_strided(const void* x, int64_t B, int64_t H, int64_t 
                                    hipStream_t stream);
 hipError_t launch_gemm(const uint8_t* xc, const uint8_t* xs, const uint8_t* wc, const uint8_t* ws, int M,
                        int N, int K, uint16_t* y, hipStream_t stream);
+hipError_t launch_qkv_gemm(const uint8_t* xc, const uint8_t* xs, const uint8_t* wc, const uint8_t* ws, int M,
+                           int K, int H, int hd, int mode, uint16_t* q, uint8_t* kc, uint8_t* ks, uint8_t* vc,
+                           uint8_t* vs, hipStream_t stream);
 hipError_t launch_varlen_table(const int* cu_seqlens, int batch, int T, int* tab, hipStream_t stream);
 hipError_t launch_quantize_varlen_cols(const void* x, int batch, int64_t T, int64_t H, int64_t d, int64_t sh,
                                        int64_t sn, const int* tab, int mode, uint8_t* codes, uint8_t* scales,
@@ -340,6 +343,51 @@ int mxgemm(const void* x, const uint8_t* wc, const uint8_t* ws, int64_t M, int64
   hipError_t e = mxattn::launch_quantize(x, 1, M, K, 1, mode, xc, xs, s);
   if (e != hipSuccess) return MXQ_ERR_HIP;
   return hip_status(mxattn::launch_gemm(xc, xs, wc, ws, int(M), int(N), int(K), static_cast<uint16_t*>(y), s));
+}
+
+int mxqkv_proj_quantized(const uint8_t* xc, const uint8_t* xs, const uint8_t* wc, const uint8_t* ws, int64_t T,
+                         int64_t C, int64_t H, int64_t d, int mode, void* q, uint8_t* kc, uint8_t* ks, uint8_t* vc,
+                         uint8_t* vs, void* stream) {
+  if (T < 1 || C < 1 || H < 1) return MXQ_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return MXQ_ERR_UNSUPPORTED;
+  if (H > (int64_t(1) << 20)) return MXQ_ERR_UNSUPPORTED;
+  int st = check_gemm_sizes(T, 3 * H * d, C);
+  if (st != MXQ_OK) return st;
+  if (check_attn_sizes(1, H, T, d) != MXQ_OK) return MXQ_ERR_UNSUPPORTED;
+  if (!valid_mode(mode)) return MXQ_ERR_INVALID_ARG;
+  if (!xc || !xs || !wc || !ws || !q || !kc || !ks || !vc || !vs) return MXQ_ERR_INVALID_ARG;
+  if (!aligned16(xc) || !aligned16(wc) || !aligned16(q) || !aligned16(kc) || !aligned16(vc))
+    return MXQ_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(xs) & 3u) || (reinterpret_cast<uintptr_t>(ws) & 3u)) return MXQ_ERR_INVALID_ARG;
+  return hip_status(mxattn::launch_qkv_gemm(xc, xs, wc, ws, int(T), int(C), int(H), int(d), mode,
+                                            static_cast<uint16_t*>(q), kc, ks, vc, vs,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int mxqkv_proj(const void* x, const uint8_t* wc, const uint8_t* ws, int64_t T, int64_t C, int64_t H, int64_t d,
+               int mode, void* q, uint8_t* kc, uint8_t* ks, uint8_t* vc, uint8_t* vs, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  if (T < 1 || C < 1 || H < 1) return MXQ_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return MXQ_ERR_UNSUPPORTED;
+  if (H > (int64_t(1) << 20)) return MXQ_ERR_UNSUPPORTED;
+  int st = check_gemm_sizes(T, 3 * H * d, C);
+  if (st != MXQ_OK) return st;
+  if (check_attn_sizes(1, H, T, d) != MXQ_OK) return MXQ_ERR_UNSUPPORTED;
+  if (!valid_mode(mode)) return MXQ_ERR_INVALID_ARG;
+  if (!x || !wc || !ws || !q || !kc || !ks || !vc || !vs) return MXQ_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(wc) || !aligned16(q) || !aligned16(kc) || !aligned16(vc))
+    return MXQ_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(ws) & 3u) return MXQ_ERR_INVALID_ARG;
+  const size_t need = mxgemm_workspace_bytes(T, C);
+  if (!workspace || workspace_bytes < need) return MXQ_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return MXQ_ERR_INVALID_ARG;
+  uint8_t* xc = static_cast<uint8_t*>(workspace);
+  uint8_t* xs = xc + round256(size_t(T * C / 2));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = mxattn::launch_quantize(x, 1, T, C, 1, mode, xc, xs, s);
+  if (e != hipSuccess) return MXQ_ERR_HIP;
+  return hip_status(mxattn::launch_qkv_gemm(xc, xs, wc, ws, int(T), int(C), int(H), int(d), mode,
+                                            static_cast<uint16_t*>(q), kc, ks, vc, vs, s));
 }
 
 int mxq_dump(const char* path, const uint8_t* codes, const uint8_t* scales, int64_t batch, int64_t nvec,

@@ -14,6 +14,15 @@
 // current step runs 64 MFMAs per wave, and one barrier per step publishes it.
 // The MFMA computes Y^T tiles (A = 16 rows of W, B = 16 rows of X), so each
 // lane ends up with four consecutive n of one m: one 8-byte store.
+//
+// QKV epilogue (the projection that feeds attention): Y's columns are
+// [Q | K | V], each H * hd wide.  The tile goes through LDS as bf16, and the
+// workgroup writes Q as bf16 [H][M][hd], K quantized along hd (codes
+// [H][M][hd/2], scales [H][M][hd/32]) and V quantized along M (codes
+// [H][hd][ceil(M/32) * 16], scales [H][hd][ceil(M/32)]): the operand layouts
+// of the attention kernel, so K and V never exist in bf16 in memory.  K and V
+// are rounded to bf16 first and quantized with the same rule and encoder as
+// mxq_quantize, so the codes equal those of the unfused path.
 #include <type_traits>
 
 #include "mx_device.h"
@@ -30,6 +39,13 @@ struct GemmArgs {
   int tn;             // tiles along N
   int ntiles;         // tiles in all
   int per_xcd;        // workgroups per XCD in the tile order below
+  // QKV epilogue only (N = 3 H hd, M = tokens of one sequence)
+  uint16_t* q;        // bf16 [H][M][hd]
+  uint8_t* kc;        // [H][M][hd/2]
+  uint8_t* ks;        // [H][M][hd/32]
+  uint8_t* vc;        // [H][hd][nbm * 16]
+  uint8_t* vs;        // [H][hd][nbm]
+  int H, hd, nbm;     // heads, head dim, ceil(M / 32)
 };
 
 constexpr int kGM = 256, kGN = 256;  // workgroup tile
@@ -73,6 +89,99 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
 
 }  // namespace
 
+namespace {
+
+// Byte address of bf16 element (r, n) of the 256 x 256 epilogue tile, which
+// reuses both operand buffers: rows 0-127 in t0, 128-255 in t1, 512 bytes per
+// row, 16-byte chunk c of row r stored at chunk c ^ (r & 31) (the 32 lanes
+// that read one chunk of 32 consecutive rows then spread over the banks).
+__device__ __forceinline__ uint8_t* tile_elem(uint8_t* t0, uint8_t* t1, int r, int n) {
+  return (r < 128 ? t0 : t1) + (r & 127) * 512 + (((n >> 3) ^ (r & 31)) << 4) + (n & 7) * 2;
+}
+
+template <int MODE>
+__device__ __forceinline__ void qkv_epilogue(const GemmArgs& a, const v4f (&acc)[8][4], GemmLds& lds0,
+                                             GemmLds& lds1, int m0, int n0, int wm, int wn, int wave,
+                                             int lane) {
+  const int r16 = lane & 15, g4 = lane >> 4;
+  uint8_t* t0 = reinterpret_cast<uint8_t*>(&lds0);
+  uint8_t* t1 = reinterpret_cast<uint8_t*>(&lds1);
+  __syncthreads();  // every wave has finished reading the operand tiles
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 64 * wm + 16 * i + r16;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int n = 128 * wn + 16 * j + 4 * g4;
+      const uint32_t b0 = f32_to_bf16_rne(acc[j][i][0]), b1 = f32_to_bf16_rne(acc[j][i][1]);
+      const uint32_t b2 = f32_to_bf16_rne(acc[j][i][2]), b3 = f32_to_bf16_rne(acc[j][i][3]);
+      *reinterpret_cast<uint2*>(tile_elem(t0, t1, r, n)) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+    }
+  }
+  __syncthreads();
+  // 64 cells of 32 rows x 32 columns; a cell lies inside one head of one of
+  // Q, K, V (H hd is a multiple of 32).  Rows past M hold zeros (their X rows
+  // read as zero), which is the padding of V's last block.
+  const int HD = a.H * a.hd, M = a.M;
+  for (int cell = wave; cell < 64; cell += kGWaves) {
+    const int cg = cell & 7, rg = cell >> 3;
+    const int n = n0 + 32 * cg;
+    if (n >= a.N) continue;
+    const int region = n / HD, nn = n - region * HD;
+    const int h = nn / a.hd, c0 = nn - h * a.hd;
+    const int rl = 32 * rg, m = m0 + rl;
+    if (region == 0 || region == 1) {
+      // Q rows, or one K block per row: two lanes per row, 16 columns each
+      const int r = lane >> 1, half = lane & 1;
+      const uint4 v0 = *reinterpret_cast<const uint4*>(tile_elem(t0, t1, rl + r, 32 * cg + 16 * half));
+      const uint4 v1 = *reinterpret_cast<const uint4*>(tile_elem(t0, t1, rl + r, 32 * cg + 16 * half + 8));
+      const int64_t row = int64_t(h) * M + m + r;
+      if (region == 0) {
+        if (m + r < M) {
+          uint4* dst = reinterpret_cast<uint4*>(a.q + row * a.hd + c0 + 16 * half);
+          dst[0] = v0;
+          dst[1] = v1;
+        }
+      } else {
+        uint32_t amax = max(absmax8_bits(v0), absmax8_bits(v1));
+        amax = max(amax, uint32_t(__builtin_amdgcn_mov_dpp(int(amax), 0xB1, 0xF, 0xF, true)));  // partner lane
+        const int e = block_exp_bf16bits<MODE>(amax);
+        const uint2 c = make_uint2(encode8_bf16(v0, e), encode8_bf16(v1, e));
+        if (m + r < M) {
+          *reinterpret_cast<uint2*>(a.kc + row * (a.hd / 2) + c0 / 2 + 8 * half) = c;
+          if (half == 0) a.ks[row * (a.hd / 32) + c0 / 32] = uint8_t(e + 127);
+        }
+      }
+    } else {
+      // one V block per column: lanes col and col + 32 take rows 0-15 and
+      // 16-31 of the block
+      const int col = lane & 31, half = lane >> 5;
+      uint32_t w[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t lo = *reinterpret_cast<const uint16_t*>(tile_elem(t0, t1, rl + 16 * half + 2 * i, 32 * cg + col));
+        const uint32_t hi = *reinterpret_cast<const uint16_t*>(tile_elem(t0, t1, rl + 16 * half + 2 * i + 1, 32 * cg + col));
+        w[i] = lo | (hi << 16);
+      }
+      const uint4 v0 = make_uint4(w[0], w[1], w[2], w[3]), v1 = make_uint4(w[4], w[5], w[6], w[7]);
+      uint32_t amax = max(absmax8_bits(v0), absmax8_bits(v1));
+      amax = max(amax, uint32_t(__shfl_xor(int(amax), 32)));
+      const int e = block_exp_bf16bits<MODE>(amax);
+      const uint2 c = make_uint2(encode8_bf16(v0, e), encode8_bf16(v1, e));
+      const int mb = m / 32;
+      if (mb < a.nbm) {
+        const int64_t vrow = int64_t(h) * a.hd + c0 + col;
+        *reinterpret_cast<uint2*>(a.vc + (vrow * a.nbm + mb) * 16 + 8 * half) = c;
+        if (half == 0) a.vs[vrow * a.nbm + mb] = uint8_t(e + 127);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+// EPI 0: Y in bf16; EPI 1: the QKV epilogue with block rule MODE.
+template <int EPI, int MODE>
 __global__ __launch_bounds__(kGWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void gemm_kernel(GemmArgs a) {
   constexpr int NT = kGWaves * 64;
   // two separate objects (not an array): the compiler then knows that the
@@ -238,6 +347,10 @@ __global__ __launch_bounds__(kGWaves * 64) __attribute__((amdgpu_waves_per_eu(2)
 
   // epilogue: acc[j][i] is the Y^T tile of W rows 128 wn + 16 j and X rows
   // 64 wm + 16 i; lane: m = r16 of it, n = 4 g4 + [0, 4)
+  if constexpr (EPI == 1) {
+    qkv_epilogue<MODE>(a, acc, lds0, lds1, m0, n0, wm, wn, wave, lane);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int m = m0 + 64 * wm + 16 * i + r16;
@@ -255,16 +368,41 @@ __global__ __launch_bounds__(kGWaves * 64) __attribute__((amdgpu_waves_per_eu(2)
   }
 }
 
-hipError_t launch_gemm(const uint8_t* xc, const uint8_t* xs, const uint8_t* wc, const uint8_t* ws, int M,
-                       int N, int K, uint16_t* y, hipStream_t stream) {
-  GemmArgs a;
-  a.xc = xc; a.xs = xs; a.wc = wc; a.ws = ws; a.y = y;
-  a.M = M; a.N = N; a.K = K;
-  const int tm = (M + kGM - 1) / kGM;
-  a.tn = (N + kGN - 1) / kGN;
+namespace {
+
+void set_tiles(GemmArgs& a) {
+  const int tm = (a.M + kGM - 1) / kGM;
+  a.tn = (a.N + kGN - 1) / kGN;
   a.ntiles = tm * a.tn;
   a.per_xcd = (a.ntiles + 7) / 8;
-  gemm_kernel<<<dim3(unsigned(a.per_xcd * 8)), dim3(kGWaves * 64), 0, stream>>>(a);
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const uint8_t* xc, const uint8_t* xs, const uint8_t* wc, const uint8_t* ws, int M,
+                       int N, int K, uint16_t* y, hipStream_t stream) {
+  GemmArgs a{};
+  a.xc = xc; a.xs = xs; a.wc = wc; a.ws = ws; a.y = y;
+  a.M = M; a.N = N; a.K = K;
+  set_tiles(a);
+  gemm_kernel<0, 0><<<dim3(unsigned(a.per_xcd * 8)), dim3(kGWaves * 64), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+// The QKV projection of one sequence of M tokens with the QKV epilogue:
+// W [3 H hd][K], outputs as in GemmArgs.
+hipError_t launch_qkv_gemm(const uint8_t* xc, const uint8_t* xs, const uint8_t* wc, const uint8_t* ws, int M,
+                           int K, int H, int hd, int mode, uint16_t* q, uint8_t* kc, uint8_t* ks, uint8_t* vc,
+                           uint8_t* vs, hipStream_t stream) {
+  GemmArgs a{};
+  a.xc = xc; a.xs = xs; a.wc = wc; a.ws = ws;
+  a.M = M; a.N = 3 * H * hd; a.K = K;
+  a.q = q; a.kc = kc; a.ks = ks; a.vc = vc; a.vs = vs;
+  a.H = H; a.hd = hd; a.nbm = (M + 31) / 32;
+  set_tiles(a);
+  const dim3 grid(unsigned(a.per_xcd * 8)), block(kGWaves * 64);
+  if (mode == kModeUOS) gemm_kernel<1, kModeUOS><<<grid, block, 0, stream>>>(a);
+  else gemm_kernel<1, kModeOCP><<<grid, block, 0, stream>>>(a);
   return hipGetLastError();
 }
 

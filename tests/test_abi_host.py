@@ -163,6 +163,34 @@ def test_varlen_workspace_and_argument_errors():
     assert fwd(ws=A + 8) == INVALID
 
 
+def test_qkv_projection_argument_errors():
+    L = mx.lib()
+    A = 1 << 20
+    pq = L.mxqkv_proj_quantized
+
+    def fq(T=300, C=256, H=3, d=64, mode=1, xc=A, xs=A, q=A, vc=A):
+        return pq(xc, xs, A, A, T, C, H, d, mode, q, A, A, vc, A, None)
+
+    assert fq(T=0) == INVALID
+    assert fq(H=0) == INVALID
+    assert fq(d=96) == UNSUPPORTED
+    assert fq(C=200) == UNSUPPORTED          # C % 128
+    assert fq(mode=4) == INVALID
+    assert fq(xc=None) == INVALID
+    assert fq(q=A + 2) == INVALID
+    assert fq(vc=A + 8) == INVALID
+    assert fq(xs=A + 2) == INVALID           # scales need 4-byte alignment
+    p = L.mxqkv_proj
+
+    def fb(T=300, C=256, H=3, d=64, ws=A, wsb=1 << 40, x=A):
+        return p(x, A, A, T, C, H, d, 1, A, A, A, A, A, ws, wsb, None)
+
+    assert fb(ws=None) == WORKSPACE
+    assert fb(wsb=L.mxgemm_workspace_bytes(300, 256) - 1) == WORKSPACE
+    assert fb(x=A + 2) == INVALID
+    assert fb(C=100) == UNSUPPORTED
+
+
 def test_dump_from_host_memory(tmp_path):
     import oracle
     import workloads
