@@ -345,10 +345,12 @@ __global__ __launch_bounds__(256) void varlen_table_kernel(const int* __restrict
   }
 }
 
-// Grid caps: the streaming kernel walks blocks with a grid stride; the column
-// kernel's workgroups each walk tiles (five 32 KiB tiles fit one CU's LDS, so
-// 2560 workgroups are two rounds of 256 CUs x 5).
-constexpr int64_t kStreamGrid = 65536;
+// Grid caps: the streaming kernel walks blocks with a grid stride (2^17
+// workgroups cover 2^30 elements in one pass; a cap of 2^16, two passes per
+// thread, ran 2^30 at 72% of HBM bandwidth against 75%); the column kernel's
+// workgroups each walk tiles (five 32 KiB tiles fit one CU's LDS, so 2560
+// workgroups are two rounds of 256 CUs x 5).
+constexpr int64_t kStreamGrid = 131072;
 constexpr int64_t kColsGrid = 2560;
 
 // Host-side launchers (stream-ordered, no allocation).  Return the HIP error
