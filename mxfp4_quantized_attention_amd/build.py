@@ -62,7 +62,26 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
     os.replace(tmp, LIB)
+    build_abi_demo(objdir)
     return LIB
+
+
+DEMO_SRC = os.path.join(ROOT, "tests", "abi_demo.c")
+DEMO = os.path.join(HERE, "_build", "abi_demo")
+
+
+def build_abi_demo(objdir: str) -> str:
+    """The plain C consumer of the library (tests/abi_demo.c): gcc, C99, HIP
+    runtime for memory and a stream, linked against libmxattn.so."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    cmd = ["gcc", "-std=c99", "-O2", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(rocm, "include"),
+           "-I", os.path.join(ROOT, "include"), DEMO_SRC, "-o", DEMO,
+           "-L", os.path.join(rocm, "lib"), "-lamdhip64", "-Wl,-rpath," + os.path.join(rocm, "lib"),
+           "-L", HERE, "-lmxattn", "-Wl,-rpath,$ORIGIN/.."]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("abi_demo build failed:\n" + r.stdout + r.stderr)
+    return DEMO
 
 
 if __name__ == "__main__":
