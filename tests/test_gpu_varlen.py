@@ -146,3 +146,18 @@ def test_wan_varlen_sampled_rows():
     rows = np.stack([toks, g.integers(0, H, toks.size)], axis=1)
     ref = oracle.attn_varlen_rows(q, k, v, cu, H, d, oracle.MODE_UOS, True, mx.kv_tile(d), 1.0 / np.sqrt(d), rows)
     compare_attention(got_all[rows[:, 0], rows[:, 1]], ref, what="wan varlen (sampled)")
+
+
+def test_many_short_sequences():
+    """More sequences than the table kernel has threads (1000 > 256), so each
+    thread scans a chunk of several entries; lengths 0..40 cover empty,
+    one-token and two-block sequences."""
+    g = np.random.default_rng(12)
+    lengths = [int(n) for n in g.integers(0, 41, 1000)]
+    H, d = 2, 64
+    q, k, v, cu = _inputs(lengths, H, d, seed=13)
+    qg, kg, vg = (to_gpu_bf16(x) for x in (q, k, v))
+    o = mx.fwd_varlen(qg, kg, vg, torch.from_numpy(cu).to("cuda:0"))
+    ref = _dense_per_sequence(qg, kg, vg, cu, "uos", True, 0.0)
+    torch.cuda.synchronize()
+    _assert_same(o, ref, cu, "1000 short sequences")
