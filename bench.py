@@ -57,11 +57,16 @@ def log(*a):
 
 
 def attn_source_hash() -> str:
+    """Identity of the attention kernel binary: its sources and the compiler
+    flags it is built with (the rest of the build script does not shape it)."""
+    from mxfp4_quantized_attention_amd import build as hip_build
     h = hashlib.sha256()
-    for path in (ATTN_SRC, os.path.join(os.path.dirname(ATTN_SRC), "mx_device.h"),
-                 os.path.join(os.path.dirname(os.path.dirname(ATTN_SRC)), "build.py")):
+    for path in (ATTN_SRC, os.path.join(os.path.dirname(ATTN_SRC), "mx_device.h")):
         with open(path, "rb") as f:
             h.update(f.read())
+    fl = hip_build.flags()
+    fl = [f for i, f in enumerate(fl) if f != "-I" and (i == 0 or fl[i - 1] != "-I")]  # paths vary by machine
+    h.update(repr((hip_build.ARCH, fl, hip_build.PER_FILE_FLAGS.get("attention.hip", []))).encode())
     return h.hexdigest()[:16]
 
 
