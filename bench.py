@@ -10,7 +10,7 @@ B=1, H=40, N=32760 (21 x 1560 tokens), d=128, UOS + PNQ, non-causal.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 
-    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--workload wan]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload wan]
 
 `--workload gemm` times the MXFP4 GEMM of a DiT linear layer instead: a
 Wan-style FFN up-projection, Y = X W^T with X [32760][5120] bf16 and W
@@ -84,6 +84,17 @@ def measured_traffic(workload: str):
     return float(t["bytes_per_launch"])
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(q, k, v, cfg, mode, pnq, kv_tile, gpu_out, heads=8, rows_per_head=3072):
     """The oracle, timed on this host's cores on a bounded sample of the same
     workload: K/V quantization of `heads` heads plus `rows_per_head` seeded
@@ -117,6 +128,7 @@ def cpu_baseline(q, k, v, cfg, mode, pnq, kv_tile, gpu_out, heads=8, rows_per_he
         "value": flop / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": oracle.num_threads(),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": f"{cfg}: K/V quantization of {heads} heads + {rows.size} seeded query rows "
                   f"({rows_per_head} per head), {dt:.1f} s; FLOP counted as 4*N*d per row",
@@ -158,8 +170,8 @@ def quality_context(q, k, v, out_uos_pnq, out_ocp, nrows=64):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="wan", choices=["tiny", "small", "wan", "hunyuan", "sweep", "gemm", "wan_varlen", "wan_block"])
     ap.add_argument("--mode", default="uos", choices=["uos", "ocp"])
     ap.add_argument("--no-pnq", action="store_true")
@@ -271,6 +283,7 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     per_kernel = np.array([[ev[i].elapsed_time(ev[i + 1]) for i in range(len(launches))] for ev in events])
     kk, kvv, ka = per_kernel.mean(axis=0)
+    ka_median = float(np.median(per_kernel[:, 2]))
     flop = 4.0 * B * H * N * N * d
     value = flop / (ms_per_step * 1e-3) / 1e12
     achieved = flop / (ka * 1e-3) / 1e12
@@ -306,7 +319,7 @@ def main():
         "pct_of_fp4_peak": 100.0 * value / PEAK_FP4_TFLOPS,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_FP4_TFLOPS, "traffic": traffic,
-                     "kernel": "attn_fwd_kernel", "kernel_ms": ka,
+                     "kernel": "attn_fwd_kernel", "kernel_ms": ka, "kernel_ms_median": ka_median,
                      "algorithmic": f"4*d FLOP per score element x B*H*N^2 = {flop:.4g} FLOP per launch"},
         "roofline_quantize": {"bound": "hbm", "unit": "GB/s", "peak": PEAK_HBM_GBS,
                               "bytes_per_launch": qbytes,
@@ -419,6 +432,7 @@ def gemm_bench(args, dev):
         ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref["out"]) + err, 1e-30))) - 7)
         result["cpu_baseline"] = {
             "value": 2.0 * rows.size * N * K / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "cpu_model": cpu_model(),
             "kind": "oracle", "seconds": dt,
             "sample": f"quantization of W and of 8192 seeded X rows, their exact product (numpy fp64), "
                       f"{dt:.1f} s; FLOP counted as 2*N*K per row",
@@ -529,7 +543,8 @@ def varlen_bench(args, dev):
         over = (diff / np.maximum(2e-3, ulp)).max(axis=1)
         flagged = ref["near_tie"]
         result["cpu_baseline"] = {
-            "value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "cpu_model": cpu_model(), "kind": "oracle",
             "seconds": dt,
             "sample": f"{rows.shape[0]} seeded (token, head) rows over heads 0..{heads - 1} with K/V quantization "
                       f"of each touched (sequence, head), {dt:.1f} s; FLOP counted as 4*N_s*d per row",
@@ -744,6 +759,7 @@ def quantize_sweep(args, dev):
         dt = time.perf_counter() - t0
         result["cpu_baseline"] = {
             "value": 2.53125 * (1 << 30) / dt / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
+            "cpu_model": cpu_model(),
             "kind": "oracle", "sample": f"UOS quantization of the 2^30 sweep values (the whole 2^30 case), {dt:.1f} s",
             "seconds": dt,
             "bit_exact_vs_gpu_on_sample": bool(np.array_equal(oc.reshape(-1), host_codes)
