@@ -124,6 +124,15 @@ def cpu_baseline(q, k, v, cfg, mode, pnq, kv_tile, gpu_out, heads=8, rows_per_he
     ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(want), 1e-30))) - 7)
     ratio = diff / np.maximum(2e-3, ulp)
     flagged = ref["near_tie"].astype(bool)
+    # one thread on a small slice of the same rows, for the per-core rate
+    threads = oracle.num_threads()
+    r1 = rows[:: max(1, rows.size // 256)][:256]
+    oracle.set_num_threads(1)
+    t1 = time.perf_counter()
+    oracle.attn_rows(qs, ks, vs, heads, N, d, mode, pnq, kv_tile, 1.0 / np.sqrt(d), r1, want_budget=False)
+    dt1 = time.perf_counter() - t1
+    oracle.set_num_threads(threads)
+    total_rows = B * H * N
     return {
         "value": flop / dt / 1e12,
         "unit": "TFLOP/s",
@@ -133,6 +142,9 @@ def cpu_baseline(q, k, v, cfg, mode, pnq, kv_tile, gpu_out, heads=8, rows_per_he
         "sample": f"{cfg}: K/V quantization of {heads} heads + {rows.size} seeded query rows "
                   f"({rows_per_head} per head), {dt:.1f} s; FLOP counted as 4*N*d per row",
         "seconds": dt,
+        "extrapolated_full_workload_seconds": dt * total_rows / rows.size,
+        "single_thread": {"value": 4.0 * N * d * r1.size / dt1 / 1e12, "unit": "TFLOP/s", "rows": int(r1.size),
+                          "seconds": dt1},
         "vs_gpu_on_sample": {
             "rel_l2": float(np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-300)),
             "max_diff_over_bound_unflagged_rows": float(ratio[~flagged].max()) if (~flagged).any() else 0.0,

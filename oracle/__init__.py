@@ -82,6 +82,8 @@ def _load():
     lib.orc_dump.restype = i32
     lib.orc_num_threads.argtypes = []
     lib.orc_num_threads.restype = i32
+    lib.orc_set_num_threads.argtypes = [i32]
+    lib.orc_set_num_threads.restype = None
     _lib = lib
     return lib
 
@@ -97,6 +99,11 @@ def _c(a, dtype):
 def num_threads() -> int:
     """OpenMP threads the oracle's row loop runs on."""
     return int(_load().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """OpenMP threads for later calls (for timing the oracle on fewer cores)."""
+    _load().orc_set_num_threads(int(n))
 
 
 def bf16_to_f64(bits) -> np.ndarray:

@@ -648,3 +648,13 @@ int orc_num_threads(void)
     return 1;
 #endif
 }
+
+/* Set the number of OpenMP threads later calls use (timing only). */
+void orc_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
