@@ -49,6 +49,15 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_FP4_TFLOPS = 10100.0  # MI355X dense MXFP4 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_wan_traffic.json")
+UTIL_FILE = os.path.join(ROOT, "profiles", "attn_fwd_wan_utilization.json")
+# The vector-unit ceiling of the attention kernel.  Every score element needs
+# one fma (scale and max shift), one exponential, half a three-input max and
+# half a two-element FP4 convert.  Measured gfx950 issue costs, in units of one
+# wave64 v_fma_f32 (1.13 ns of a SIMD): exp 3.2, FP4 convert 4.1 per two
+# elements, max3 1.6 per two elements; 1024 SIMDs.
+VALU_SLOTS_PER_SCORE = 1.0 + 3.2 + 4.1 / 2 + 1.6 / 2
+VALU_SLOT_NS = 1.13
+N_SIMDS = 1024
 ATTN_SRC = os.path.join(ROOT, "mxfp4_quantized_attention_amd", "csrc", "attention.hip")
 
 
@@ -82,6 +91,36 @@ def measured_traffic(workload: str):
     if t.get("kernel_sha") != attn_source_hash() or t.get("workload") != workload:
         return None
     return float(t["bytes_per_launch"])
+
+
+def valu_ceiling_tflops(d: int) -> float:
+    """FLOP/s (4 d per score element) at which the per-score vector work alone
+    would fill every SIMD's issue slots."""
+    scores_per_s = N_SIMDS * 64 / (VALU_SLOTS_PER_SCORE * VALU_SLOT_NS * 1e-9)
+    return 4.0 * d * scores_per_s / 1e12
+
+
+def measured_utilization(workload: str):
+    """MFMA-busy and VALU-active fractions of the attention launch from the
+    committed rocprofv3 counter summary (None if taken on another kernel
+    version or workload)."""
+    try:
+        with open(UTIL_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sha") != attn_source_hash() or t.get("workload") != workload:
+        return None
+    return t
+
+
+def valu_bound(achieved: float, d: int, workload: str) -> dict:
+    ceiling = valu_ceiling_tflops(d)
+    util = measured_utilization(workload)
+    return {"bound": "valu", "ceiling": ceiling, "unit": "TFLOP/s", "frac": achieved / ceiling,
+            "slots_per_score": VALU_SLOTS_PER_SCORE, "slot_ns": VALU_SLOT_NS,
+            "valu_active": util["valu_active"] if util else None,
+            "mfma_busy": util["mfma_busy"] if util else None}
 
 
 def cpu_model() -> str:
@@ -333,6 +372,7 @@ def main():
                      "frac": achieved / PEAK_FP4_TFLOPS, "traffic": traffic,
                      "kernel": "attn_fwd_kernel", "kernel_ms": ka, "kernel_ms_median": ka_median,
                      "algorithmic": f"4*d FLOP per score element x B*H*N^2 = {flop:.4g} FLOP per launch"},
+        "valu_bound": valu_bound(achieved, d, args.workload),
         "roofline_quantize": {"bound": "hbm", "unit": "GB/s", "peak": PEAK_HBM_GBS,
                               "bytes_per_launch": qbytes,
                               "k_axis1_ms": kk, "k_axis1_gbs": qbytes / (kk * 1e-3) / 1e9,
