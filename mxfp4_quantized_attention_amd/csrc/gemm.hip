@@ -124,10 +124,49 @@ __device__ __forceinline__ void qkv_epilogue(const GemmArgs& a, const v4f (&acc)
     }
   }
   __syncthreads();
-  // 64 cells of 32 rows x 32 columns; a cell lies inside one head of one of
-  // Q, K, V (H hd is a multiple of 32).  Rows past M hold zeros (their X rows
-  // read as zero), which is the padding of V's last block.
   const int HD = a.H * a.hd, M = a.M;
+  const int region0 = n0 / HD, region1 = (min(n0 + kGN, a.N) - 1) / HD;
+  if (region0 == region1 && region0 == 0) {
+    // A tile of Q only: whole tile rows, 32 lanes x 16 bytes each, two rows
+    // per instruction (a 16-byte chunk never straddles a head: hd % 8 == 0)
+    const int cc = lane & 31, n = n0 + 8 * cc;
+    const int h = n / a.hd, c0 = n - h * a.hd;
+#pragma unroll 4
+    for (int k = 0; k < 16; ++k) {
+      const int r = 32 * wave + 2 * k + (lane >> 5), m = m0 + r;
+      if (m >= M || n >= a.N) continue;
+      const v4u v = *reinterpret_cast<const v4u*>(tile_elem(t0, t1, r, 8 * cc));
+      __builtin_nontemporal_store(v, reinterpret_cast<v4u*>(a.q + (int64_t(h) * M + m) * a.hd + c0));
+    }
+    return;
+  }
+  if (region0 == region1 && region0 == 1) {
+    // A tile of K only: one 32-value block per lane, eight rows of eight
+    // blocks per instruction, so the lanes of one head's row write its code
+    // bytes contiguously
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int idx = (4 * wave + it) * 64 + lane, r = idx >> 3, b = idx & 7;
+      const int m = m0 + r, n = n0 + 32 * b;
+      uint4 v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = *reinterpret_cast<const uint4*>(tile_elem(t0, t1, r, 32 * b + 8 * q));
+      const uint32_t amax = max(max(absmax8_bits(v[0]), absmax8_bits(v[1])), max(absmax8_bits(v[2]), absmax8_bits(v[3])));
+      const int e = block_exp_bf16bits<MODE>(amax);
+      if (m < M && n < a.N) {
+        const int nn = n - HD, h = nn / a.hd, c0 = nn - h * a.hd;
+        const int64_t row = int64_t(h) * M + m;
+        *reinterpret_cast<uint4*>(a.kc + row * (a.hd / 2) + c0 / 2) =
+            make_uint4(encode8_bf16(v[0], e), encode8_bf16(v[1], e), encode8_bf16(v[2], e), encode8_bf16(v[3], e));
+        a.ks[row * (a.hd / 32) + c0 / 32] = uint8_t(e + 127);
+      }
+    }
+    return;
+  }
+  // Otherwise (V, or a tile that straddles regions): 64 cells of 32 rows x
+  // 32 columns; a cell lies inside one head of one of Q, K, V (H hd is a
+  // multiple of 32).  Rows past M hold zeros (their X rows read as zero),
+  // which is the padding of V's last block.
   for (int cell = wave; cell < 64; cell += kGWaves) {
     const int cg = cell & 7, rg = cell >> 3;
     const int n = n0 + 32 * cg;
