@@ -49,6 +49,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_FP4_TFLOPS = 10100.0  # MI355X dense MXFP4 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_wan_traffic.json")
+GEMM_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_dit_ffn_traffic.json")
 UTIL_FILE = os.path.join(ROOT, "profiles", "attn_fwd_wan_utilization.json")
 # The vector-unit ceiling of the attention kernel.  Every score element needs
 # one fma (scale and max shift), one exponential, half a three-input max and
@@ -65,32 +66,55 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def attn_source_hash() -> str:
-    """Identity of the attention kernel binary: its sources and the compiler
-    flags it is built with (the rest of the build script does not shape it)."""
+def source_hash(src: str = "attention.hip") -> str:
+    """Identity of one kernel source's binary: the file, the shared device
+    header and the compiler flags it is built with (the rest of the build
+    script does not shape it)."""
     from mxfp4_quantized_attention_amd import build as hip_build
     h = hashlib.sha256()
-    for path in (ATTN_SRC, os.path.join(os.path.dirname(ATTN_SRC), "mx_device.h")):
+    csrc = os.path.dirname(ATTN_SRC)
+    for path in (os.path.join(csrc, src), os.path.join(csrc, "mx_device.h")):
         with open(path, "rb") as f:
             h.update(f.read())
     fl = hip_build.flags()
     fl = [f for i, f in enumerate(fl) if f != "-I" and (i == 0 or fl[i - 1] != "-I")]  # paths vary by machine
-    h.update(repr((hip_build.ARCH, fl, hip_build.PER_FILE_FLAGS.get("attention.hip", []))).encode())
+    h.update(repr((hip_build.ARCH, fl, hip_build.PER_FILE_FLAGS.get(src, []))).encode())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per attention launch from the committed rocprofv3 counter
-    summary, or None when the counters were taken on another kernel version or
-    workload."""
+def attn_source_hash() -> str:
+    return source_hash("attention.hip")
+
+
+def measured_traffic(workload: str, path: str = TRAFFIC_FILE, src: str = "attention.hip"):
+    """HBM bytes per launch of the dominant kernel from a committed rocprofv3
+    counter summary, or None when the counters were taken on another kernel
+    version or workload."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_sha") != attn_source_hash() or t.get("workload") != workload:
+    if t.get("kernel_sha") != source_hash(src) or t.get("workload") != workload:
         return None
     return float(t["bytes_per_launch"])
+
+
+def copy_calibration(mib: int, dev) -> None:
+    """A plain elementwise copy kernel of known size (reads and writes mib MiB
+    each): the reference that scales rocprofv3's FETCH_SIZE and WRITE_SIZE
+    counters to bytes."""
+    import torch
+    nbytes = mib << 20
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    flush = torch.ones(2 * nbytes // 4, dtype=torch.float32, device=dev)  # evict src from the caches
+    del flush
+    torch.cuda.synchronize()
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    log(f"[bench] calibration copy kernel: {nbytes} bytes read, {nbytes} bytes written")
+    del src, dst
 
 
 def valu_ceiling_tflops(d: int) -> float:
@@ -305,19 +329,7 @@ def main():
             ev[len(launches)].record(stream)
 
     if args.copy_calibration_mib:
-        # a plain elementwise copy kernel of known size (reads and writes
-        # nbytes each): the reference that scales rocprofv3's FETCH_SIZE and
-        # WRITE_SIZE counters to bytes
-        nbytes = args.copy_calibration_mib << 20
-        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        flush = torch.ones(2 * nbytes // 4, dtype=torch.float32, device=dev)  # evict src from the caches
-        del flush
-        torch.cuda.synchronize()
-        torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        log(f"[bench] calibration copy kernel: {nbytes} bytes read, {nbytes} bytes written")
-        del src, dst
+        copy_calibration(args.copy_calibration_mib, dev)
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
@@ -434,6 +446,8 @@ def gemm_bench(args, dev):
         if ev is not None:
             ev[len(launches)].record(stream)
 
+    if args.copy_calibration_mib:
+        copy_calibration(args.copy_calibration_mib, dev)
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
@@ -466,7 +480,8 @@ def gemm_bench(args, dev):
                    "mode": args.mode, "parallelism": "single GPU"},
         "pct_of_fp4_peak": 100.0 * value / PEAK_FP4_TFLOPS,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_FP4_TFLOPS, "traffic": None, "kernel": "gemm_kernel",
+                     "frac": achieved / PEAK_FP4_TFLOPS,
+                     "traffic": measured_traffic("gemm", GEMM_TRAFFIC_FILE, "gemm.hip"), "kernel": "gemm_kernel",
                      "kernel_ms": kg, "algorithmic": f"2*M*N*K = {flop:.4g} FLOP per launch"},
         "quantize_x_ms": kx,
         "step_equals_mxgemm": same,
