@@ -5,8 +5,9 @@ The fused kernel must equal the unfused path bit for bit: mxgemm_quantized
 to bf16 Y = [Q | K | V], then Q rearranged to [H][T][d], K quantized along d
 and V along T with mxq_quantize_strided (which the quantizer tests pin
 against the oracle bit for bit, and which a direct oracle check repeats here
-on a small shape).  Shapes cover tiles that straddle the Q/K/V boundaries
-(3*H*d not a multiple of 256), ragged T (partial last V block and partial
+on a small shape).  Shapes cover tiles that lie wholly inside Q, K or V
+(H*d a multiple of 256, written as whole tiles) and tiles that straddle the
+Q/K/V boundaries (written cell by cell), ragged T (partial last V block and partial
 last tile), both head dims and both scale rules, and the Wan attention block
 (T = 32760, C = 5120, H = 40, d = 128).  End to end, projection plus
 mxattn_fwd_kv_quantized equals mxattn_fwd on the bf16 Q, K, V of the unfused
@@ -25,7 +26,10 @@ if HAVE_GPU:
     import torch
     import mxfp4_quantized_attention_amd as mx
 
-SHAPES = [(300, 256, 3, 64), (1000, 512, 2, 128), (257, 128, 5, 64), (64, 384, 1, 128), (513, 640, 4, 128)]
+# H*d = 256 or 512 give tiles that lie wholly inside Q, K or V (the whole-tile
+# writers); 192 and 320 give tiles that straddle two regions (the cell walk)
+SHAPES = [(300, 256, 3, 64), (1000, 512, 2, 128), (257, 128, 5, 64), (64, 384, 1, 128), (513, 640, 4, 128),
+          (260, 384, 4, 64), (33, 256, 8, 64)]
 
 
 def up(bits):
@@ -72,8 +76,8 @@ def test_fused_equals_unfused(T, C, H, d, mode):
 
 
 @pytest.mark.parametrize("mode,omode", [("uos", oracle.MODE_UOS), ("ocp", oracle.MODE_OCP)])
-def test_fused_codes_match_oracle_quantizer(mode, omode):
-    T, C, H, d = 300, 256, 3, 64
+@pytest.mark.parametrize("T,C,H,d", [(300, 256, 3, 64), (260, 384, 4, 64)])
+def test_fused_codes_match_oracle_quantizer(mode, omode, T, C, H, d):
     _, xc, xs, wc, ws = _project(T, C, H, d, mode, seed=5)
     q, kc, ks, vc, vs = mx.qkv_proj_quantized(xc, xs, wc, ws, T, C, H, d, mode=mode)
     y = mx.gemm_quantized(xc, xs, wc, ws, T, 3 * H * d, C)
