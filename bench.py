@@ -166,6 +166,7 @@ def cpu_baseline(q, k, v, cfg, mode, pnq, kv_tile, gpu_out, heads=8, rows_per_he
     import oracle
     import workloads
     B, H, N, d = q.shape
+    heads, rows_per_head = min(heads, B * H), min(rows_per_head, N)
     rows = []
     g = np.random.default_rng(11)
     for h in range(heads):
@@ -399,7 +400,10 @@ def main():
         result["quality"] = quality_context(q, k, v, gpu_out, out_ocp)
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
-        result["cpu_baseline"] = cpu_baseline(q, k, v, args.workload, mode, pnq, mx.kv_tile(d), gpu_out)
+        # the small configurations are timed in full, the large ones on a sample
+        full = args.workload in ("tiny", "small")
+        result["cpu_baseline"] = cpu_baseline(q, k, v, args.workload, mode, pnq, mx.kv_tile(d), gpu_out,
+                                              **({"heads": B * H, "rows_per_head": N} if full else {}))
     print(json.dumps(result), flush=True)
 
 
