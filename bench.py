@@ -144,7 +144,8 @@ def valu_bound(achieved: float, d: int, workload: str) -> dict:
     return {"bound": "valu", "ceiling": ceiling, "unit": "TFLOP/s", "frac": achieved / ceiling,
             "slots_per_score": VALU_SLOTS_PER_SCORE, "slot_ns": VALU_SLOT_NS,
             "valu_active": util["valu_active"] if util else None,
-            "mfma_busy": util["mfma_busy"] if util else None}
+            "mfma_busy": util["mfma_busy"] if util else None,
+            "clock_ghz_profiled": util["clock_ghz"] if util else None}
 
 
 def cpu_model() -> str:
