@@ -67,3 +67,21 @@ def test_custom_op_matches_binding():
     torch.cuda.synchronize()
     assert o1.shape == q.shape and o1.stride() == q.stride()
     assert same_bits(o1, o2)
+
+
+def test_custom_op_fake_and_compile():
+    """The operator's fake implementation agrees with the real one (shape,
+    dtype, strides) under torch.library.opcheck, and a torch.compile'd caller
+    (aot_eager: graph capture, no code generation) returns the same bits."""
+    import mxfp4_quantized_attention_amd.torch_ops  # noqa: F401
+    q, k, v = (rand_bf16((1, 130, 2, 64), seed=20 + i).transpose(1, 2) for i in range(3))
+    torch.library.opcheck(torch.ops.mxfp4_attn.attention.default, (q, k, v, "uos", True, 0.0),
+                          test_utils=("test_schema", "test_faketensor"))
+
+    def f(q, k, v):
+        return torch.ops.mxfp4_attn.attention(q, k, v, "ocp", False, 0.0) * 1.0
+
+    o1 = torch.compile(f, backend="aot_eager", fullgraph=True)(q, k, v)
+    o2 = mx.fwd_strided(q, k, v, mode="ocp", pnq=False)
+    torch.cuda.synchronize()
+    assert o1.shape == q.shape and same_bits(o1, o2)
