@@ -35,7 +35,10 @@
  *     run on the host before anything is enqueued, so a rejected call has no
  *     effect; a failed launch is reported as MXQ_ERR_HIP.
  *   - Inputs must be finite bf16 values (non-finite input is a precondition
- *     violation; the results are then unspecified).
+ *     violation; the results are then unspecified).  Attention scores and
+ *     GEMM outputs are accumulated in fp32, so they must also fit fp32: a
+ *     product of the dequantized operands that overflows fp32 is outside the
+ *     supported range.
  *   - The library keeps no global state; calls on different streams may run
  *     concurrently as long as they do not write the same buffers.
  */
