@@ -81,6 +81,18 @@ def test_large_sampled(name):
         compare_attention(got, ref, what=f"{name} {gmode} pnq={pnq} (512 rows)")
 
 
+def test_long_sequence_sampled():
+    """A quarter-million-token head (2048 key tiles, 8192 32-key V blocks
+    per channel, index arithmetic far past the benchmark shapes), N odd so
+    the last query and key tiles are ragged, on 64 sampled query rows."""
+    B, H, N, d = 1, 1, 262143, 64
+    q, k, v = workloads.qkv("tiny", B=B, H=H, N=N, d=d)
+    rows = workloads.sample_rows(B * H, N, 64)
+    got = run_gpu(q, k, v, "uos", True)[rows]
+    ref = run_oracle(q, k, v, oracle.MODE_UOS, True, rows)
+    compare_attention(got, ref, what=f"long sequence N={N} (64 rows)")
+
+
 @pytest.mark.parametrize("N,d", [(256, 64), (1000, 128), (4100, 64)])
 @pytest.mark.parametrize("omode,gmode,pnq", COMBOS)
 def test_exponentials_on_rounding_ties(N, d, omode, gmode, pnq):
