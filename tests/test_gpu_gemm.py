@@ -53,7 +53,7 @@ def run_gemm(x, w, M, N, K, gmode):
 
 @pytest.mark.parametrize("omode,gmode", MODES)
 @pytest.mark.parametrize("M,N,K", [(256, 256, 256), (300, 260, 384), (1, 4, 128), (513, 768, 640),
-                                   (1000, 1000, 1024), (64, 520, 2048), (700, 300, 128)])
+                                   (1000, 1000, 1024), (64, 520, 2048), (700, 300, 128), (70, 264, 20480)])
 def test_gemm_full(omode, gmode, M, N, K):
     x, w = workloads.gemm_inputs(M=M, N=N, K=K, seed=M + N + K)
     y, _ = run_gemm(x, w, M, N, K, gmode)
