@@ -829,13 +829,24 @@ def quantize_sweep(args, dev):
         t0 = time.perf_counter()
         oc, os_ = oracle.quantize_bf16(xh.reshape(1, 1 << 20, 1024), 1, 1 << 20, 1024, 1, oracle.MODE_UOS)
         dt = time.perf_counter() - t0
+        same = bool(np.array_equal(oc.reshape(-1), host_codes) and np.array_equal(os_.reshape(-1), host_scales))
+        del xh, oc, os_
+        # the smaller sizes, each timed in full as well
+        per_size = []
+        for p in (20, 22, 24, 26, 28):
+            xp = workloads.sweep(p)
+            t1 = time.perf_counter()
+            oracle.quantize_bf16(xp.reshape(1, 1 << (p - 10), 1024), 1, 1 << (p - 10), 1024, 1, oracle.MODE_UOS)
+            d1 = time.perf_counter() - t1
+            per_size.append({"p": p, "seconds": d1, "value": 2.53125 * (1 << p) / d1 / 1e9})
+        per_size.append({"p": 30, "seconds": dt, "value": 2.53125 * (1 << 30) / dt / 1e9})
         result["cpu_baseline"] = {
             "value": 2.53125 * (1 << 30) / dt / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
             "cpu_model": cpu_model(),
             "kind": "oracle", "sample": f"UOS quantization of the 2^30 sweep values (the whole 2^30 case), {dt:.1f} s",
             "seconds": dt,
-            "bit_exact_vs_gpu_on_sample": bool(np.array_equal(oc.reshape(-1), host_codes)
-                                               and np.array_equal(os_.reshape(-1), host_scales)),
+            "per_size": per_size,
+            "bit_exact_vs_gpu_on_sample": same,
         }
     print(json.dumps(result), flush=True)
 
