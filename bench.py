@@ -207,6 +207,7 @@ def cpu_baseline(q, k, v, cfg, mode, pnq, kv_tile, gpu_out, heads=8, rows_per_he
         "sample": f"{cfg}: K/V quantization of {heads} heads + {rows.size} seeded query rows "
                   f"({rows_per_head} per head), {dt:.1f} s; FLOP counted as 4*N*d per row",
         "seconds": dt,
+        "rows_per_second": rows.size / dt,
         "extrapolated_full_workload_seconds": dt * total_rows / rows.size,
         "single_thread": {"value": 4.0 * N * d * r1.size / dt1 / 1e12, "unit": "TFLOP/s", "rows": int(r1.size),
                           "seconds": dt1},
