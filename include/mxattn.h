@@ -294,8 +294,10 @@ int mxqkv_proj(const void *x, const uint8_t *wc, const uint8_t *ws, int64_t T, i
  * scale bytes in the canonical layout (nvec = vectors per batch entry, L =
  * their length: rows/cols for axis 1, cols/rows for axis 0).
  * codes/scales may be device pointers (copied on `stream`, which is then
- * synchronized) or host pointers (read directly).  Synchronous.
- * Errors: MXQ_ERR_INVALID_ARG, MXQ_ERR_HIP (copy failed), MXQ_ERR_IO.
+ * synchronized) or host pointers (read directly), both of the same kind.
+ * Synchronous.
+ * Errors: MXQ_ERR_INVALID_ARG (also for one device and one host pointer),
+ * MXQ_ERR_HIP (copy failed), MXQ_ERR_IO.
  */
 int mxq_dump(const char *path, const uint8_t *codes, const uint8_t *scales, int64_t batch,
              int64_t nvec, int64_t L, int axis, int mode, void *stream);

@@ -128,6 +128,71 @@ def _bf16_device(t, name):
     return t
 
 
+# Argument checks of the binding.  The C ABI sees only pointers, so a host
+# tensor, a tensor on another GPU or an undersized output would reach the
+# kernels as a bad address; every entry point checks its tensors here first
+# and raises before anything is enqueued.
+
+def _on_one_gpu(named):
+    """named: (tensor, name) pairs.  Every tensor must be a CUDA tensor, all
+    on one device; returns that device."""
+    import torch
+    dev = None
+    for t, n in named:
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise TypeError(f"{n} must be a CUDA tensor")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{n} is on {t.device}, expected {dev} like the other operands")
+    return dev
+
+
+def _u8_operand(t, name, need: int):
+    """A quantized operand (codes or scales): contiguous uint8 with at least
+    `need` bytes."""
+    import torch
+    if t.dtype != torch.uint8:
+        raise TypeError(f"{name} must be a uint8 tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < need:
+        raise ValueError(f"{name} holds {t.numel()} bytes, needs {need}")
+    return t
+
+
+def _check_out(out, shape, dev, name="out", dense=True):
+    """An output tensor given by the caller: bf16, on `dev`, of `shape`; dense
+    entry points also need it contiguous, strided ones a contiguous last dim."""
+    import torch
+    if not isinstance(out, torch.Tensor) or not out.is_cuda:
+        raise TypeError(f"{name} must be a CUDA tensor")
+    if out.device != dev:
+        raise ValueError(f"{name} is on {out.device}, expected {dev}")
+    if out.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16")
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(out.shape)}, expected {tuple(shape)}")
+    if dense and not out.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not dense and out.dim() > 0 and out.numel() > 0 and out.stride(-1) != 1:
+        raise ValueError(f"{name} needs a contiguous last dimension")
+    return out
+
+
+def _workspace(ws, need: int, dev):
+    import torch
+    if ws is None:
+        return torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if not isinstance(ws, torch.Tensor) or not ws.is_cuda or ws.device != dev:
+        raise TypeError(f"workspace must be a CUDA tensor on {dev}")
+    if ws.dtype != torch.uint8 or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+    if ws.numel() < need:
+        raise ValueError(f"workspace holds {ws.numel()} bytes, needs {need}")
+    return ws
+
+
 def n_blocks(L: int) -> int:
     return (L + 31) // 32
 
@@ -144,6 +209,8 @@ def quantize(x, mode="uos", axis: int = 1):
     x = _bf16_device(x, "x")
     if x.dim() < 2:
         raise ValueError("x needs at least 2 dimensions")
+    if axis not in (0, 1):
+        raise ValueError(f"axis must be 0 or 1, got {axis!r}")
     rows, cols = x.shape[-2], x.shape[-1]
     batch = x.numel() // max(1, rows * cols) if rows * cols else math.prod(x.shape[:-2])
     nvec, L = (rows, cols) if axis == 1 else (cols, rows)
@@ -155,17 +222,34 @@ def quantize(x, mode="uos", axis: int = 1):
     return codes, scales
 
 
-def fwd(q, k, v, mode="uos", pnq: bool = True, softmax_scale: float = 0.0, workspace=None, out=None):
-    """Non-causal MXFP4 attention.  q, k, v: bf16 [B, H, N, d] -> o bf16 [B, H, N, d]."""
-    import torch
+def _qkv4(q, k, v):
+    """Dense bf16 [B, H, N, d] Q, K, V on one GPU; returns (B, H, N, d, device)."""
+    dev = _on_one_gpu(((q, "q"), (k, "k"), (v, "v")))
     q, k, v = (_bf16_device(t, n) for t, n in ((q, "q"), (k, "k"), (v, "v")))
     if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
         raise ValueError("q, k, v must all be [B, H, N, d]")
-    B, H, N, d = q.shape
-    need = workspace_bytes(B, H, N, d)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    o = torch.empty_like(q) if out is None else out
+    return (*q.shape, dev)
+
+
+def _kv_operands(kc, ks, vc, vs, B, H, N, d, dev):
+    """K quantized along d and V along N in the canonical layouts (batch B*H)."""
+    _on_one_gpu(((kc, "kc"), (ks, "ks"), (vc, "vc"), (vs, "vs")))
+    for t, n in ((kc, "kc"), (ks, "ks"), (vc, "vc"), (vs, "vs")):
+        if t.device != dev:
+            raise ValueError(f"{n} is on {t.device}, expected {dev}")
+    BH, nbn = B * H, n_blocks(N)
+    _u8_operand(kc, "kc", BH * N * (d // 2))
+    _u8_operand(ks, "ks", BH * N * (d // 32))
+    _u8_operand(vc, "vc", BH * d * nbn * 16)
+    _u8_operand(vs, "vs", BH * d * nbn)
+
+
+def fwd(q, k, v, mode="uos", pnq: bool = True, softmax_scale: float = 0.0, workspace=None, out=None):
+    """Non-causal MXFP4 attention.  q, k, v: bf16 [B, H, N, d] -> o bf16 [B, H, N, d]."""
+    import torch
+    B, H, N, d, dev = _qkv4(q, k, v)
+    workspace = _workspace(workspace, workspace_bytes(B, H, N, d), dev)
+    o = torch.empty_like(q) if out is None else _check_out(out, q.shape, dev)
     _check(lib().mxattn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, N, d, _mode(mode),
                             int(bool(pnq)), float(softmax_scale), o.data_ptr(), workspace.data_ptr(),
                             workspace.numel(), _stream(q)), "mxattn_fwd")
@@ -177,7 +261,12 @@ def fwd_quantized(qc, qs, kc, ks, vc, vs, B: int, H: int, N: int, d: int, mode="
     """The fused kernel on operands already quantized by ``quantize`` (Q, K along
     d with axis 1; V along N with axis 0, batch = B*H)."""
     import torch
-    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=qc.device) if out is None else out
+    dev = _on_one_gpu(((qc, "qc"), (qs, "qs")))
+    _u8_operand(qc, "qc", B * H * N * (d // 2))
+    _u8_operand(qs, "qs", B * H * N * (d // 32))
+    _kv_operands(kc, ks, vc, vs, B, H, N, d, dev)
+    shape = (B, H, N, d)
+    o = torch.empty(shape, dtype=torch.bfloat16, device=dev) if out is None else _check_out(out, shape, dev)
     _check(lib().mxattn_fwd_quantized(qc.data_ptr(), qs.data_ptr(), kc.data_ptr(), ks.data_ptr(),
                                       vc.data_ptr(), vs.data_ptr(), B, H, N, d, _mode(mode),
                                       int(bool(pnq)), float(softmax_scale), o.data_ptr(), _stream(qc)),
@@ -191,10 +280,13 @@ def fwd_kv_quantized(q, kc, ks, vc, vs, mode="uos", pnq: bool = True, softmax_sc
     kernel), K and V already quantized by ``quantize`` (K along d with axis 1,
     V along N with axis 0, batch = B*H)."""
     import torch
-    if q.dtype != torch.bfloat16 or q.dim() != 4 or not q.is_contiguous():
+    dev = _on_one_gpu(((q, "q"),))
+    q = _bf16_device(q, "q")
+    if q.dim() != 4:
         raise ValueError("q must be a contiguous bf16 [B, H, N, d] tensor")
     B, H, N, d = q.shape
-    o = torch.empty_like(q) if out is None else out
+    _kv_operands(kc, ks, vc, vs, B, H, N, d, dev)
+    o = torch.empty_like(q) if out is None else _check_out(out, q.shape, dev)
     _check(lib().mxattn_fwd_kv_quantized(q.data_ptr(), kc.data_ptr(), ks.data_ptr(), vc.data_ptr(),
                                          vs.data_ptr(), B, H, N, d, _mode(mode), int(bool(pnq)),
                                          float(softmax_scale), o.data_ptr(), _stream(q)),
@@ -214,19 +306,20 @@ def fwd_strided(q, k, v, mode="uos", pnq: bool = True, softmax_scale: float = 0.
     a packed QKV tensor.  O gets q's strides when q is dense in some order
     (torch.empty_like), else the dense [B, H, N, d] layout."""
     import torch
+    dev = _on_one_gpu(((q, "q"), (k, "k"), (v, "v")))
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         if t.dtype != torch.bfloat16:
             raise ValueError(f"{n} must be bf16")
-    if q.shape != k.shape or q.shape != v.shape:
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
         raise ValueError("q, k and v must have the same [B, H, N, d] shape")
     B, H, N, d = q.shape
     if out is None:
         out = torch.empty_like(q)
         if out.stride(3) != 1:
             out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
-    need = workspace_bytes(B, H, N, d)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    else:
+        _check_out(out, q.shape, dev, dense=False)
+    workspace = _workspace(workspace, workspace_bytes(B, H, N, d), dev)
     _check(lib().mxattn_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, d,
                                     _strides3(q, "q"), _strides3(k, "k"), _strides3(v, "v"), _strides3(out, "out"),
                                     _mode(mode), int(bool(pnq)), float(softmax_scale), workspace.data_ptr(),
@@ -246,6 +339,7 @@ def fwd_varlen(q, k, v, cu_seqlens, mode="uos", pnq: bool = True, softmax_scale:
     one mxattn_fwd call per sequence, bit for bit.  O is allocated like q
     (tokens outside every sequence are left as allocated) unless given."""
     import torch
+    dev = _on_one_gpu(((q, "q"), (k, "k"), (v, "v"), (cu_seqlens, "cu_seqlens")))
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         if t.dtype != torch.bfloat16:
             raise ValueError(f"{n} must be bf16")
@@ -255,17 +349,17 @@ def fwd_varlen(q, k, v, cu_seqlens, mode="uos", pnq: bool = True, softmax_scale:
         raise ValueError("q, k and v must have the same [T, H, d] shape")
     if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous():
         raise ValueError("cu_seqlens must be a contiguous 1-D int32 tensor")
-    if cu_seqlens.device != q.device:
-        raise ValueError("cu_seqlens must be on q's device")
+    if cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens needs at least 2 entries (one sequence)")
     T, H, d = q.shape
     batch = cu_seqlens.numel() - 1
     if out is None:
         out = torch.empty_like(q)
         if out.stride(2) != 1:
             out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
-    need = varlen_workspace_bytes(batch, T, H, d)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    else:
+        _check_out(out, q.shape, dev, dense=False)
+    workspace = _workspace(workspace, varlen_workspace_bytes(batch, T, H, d), dev)
     st = (ctypes.c_int64 * 8)(q.stride(0), q.stride(1), k.stride(0), k.stride(1), v.stride(0), v.stride(1),
                               out.stride(0), out.stride(1))
     _check(lib().mxattn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), cu_seqlens.data_ptr(),
@@ -278,6 +372,11 @@ def quantize_strided(x, mode="uos", axis: int = 1):
     """mxq_quantize of a [B, H, rows, cols]-shaped view with contiguous cols
     (cols % 32 == 0); returns canonical (codes, scales) with batch B*H."""
     import torch
+    _on_one_gpu(((x, "x"),))
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    if axis not in (0, 1):
+        raise ValueError(f"axis must be 0 or 1, got {axis!r}")
     B, H, R, C = x.shape
     L = C if axis == 1 else R
     nv = R if axis == 1 else C
@@ -289,11 +388,24 @@ def quantize_strided(x, mode="uos", axis: int = 1):
     return codes, scales
 
 
+def _gemm_weights(wc, ws, N, K, dev):
+    for t, n in ((wc, "wc"), (ws, "ws")):
+        _on_one_gpu(((t, n),))
+        if t.device != dev:
+            raise ValueError(f"{n} is on {t.device}, expected {dev}")
+    _u8_operand(wc, "wc", N * (K // 2))
+    _u8_operand(ws, "ws", N * (K // 32))
+
+
 def gemm_quantized(xc, xs, wc, ws, M: int, N: int, K: int, out=None):
     """Y = X W^T on operands quantized by ``quantize`` (X [M][K] and W [N][K],
     batch 1, axis 1); returns bf16 [M, N]."""
     import torch
-    y = torch.empty((M, N), dtype=torch.bfloat16, device=xc.device) if out is None else out
+    dev = _on_one_gpu(((xc, "xc"), (xs, "xs")))
+    _u8_operand(xc, "xc", M * (K // 2))
+    _u8_operand(xs, "xs", M * (K // 32))
+    _gemm_weights(wc, ws, N, K, dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if out is None else _check_out(out, (M, N), dev)
     _check(lib().mxgemm_quantized(xc.data_ptr(), xs.data_ptr(), wc.data_ptr(), ws.data_ptr(), M, N, K,
                                   y.data_ptr(), _stream(xc)), "mxgemm_quantized")
     return y
@@ -303,15 +415,16 @@ def gemm(x, wc, ws, N: int, mode="uos", out=None, workspace=None):
     """Y = X W^T with bf16 X [M, K] quantized on the fly and W already
     quantized (codes, scales of W [N][K], axis 1)."""
     import torch
+    dev = _on_one_gpu(((x, "x"),))
     if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
         raise ValueError("x must be a contiguous bf16 [M, K] tensor")
     M, K = x.shape
+    _gemm_weights(wc, ws, N, K, dev)
     need = int(lib().mxgemm_workspace_bytes(M, K))
     if need == 0:
         raise ValueError(f"unsupported GEMM shape M={M} K={K} (K must be a positive multiple of 128)")
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
-    y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device) if out is None else out
+    workspace = _workspace(workspace, need, dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if out is None else _check_out(out, (M, N), dev)
     _check(lib().mxgemm(x.data_ptr(), wc.data_ptr(), ws.data_ptr(), M, N, K, _mode(mode), y.data_ptr(),
                         workspace.data_ptr(), workspace.numel(), _stream(x)), "mxgemm")
     return y
@@ -329,7 +442,11 @@ def _qkv_outputs(T, H, d, dev):
 def qkv_proj_quantized(xc, xs, wc, ws, T: int, C: int, H: int, d: int, mode="uos"):
     """mxqkv_proj_quantized: returns (q [1, H, T, d] bf16, kc, ks, vc, vs) in
     the layouts fwd_kv_quantized takes with B = 1, N = T."""
-    q, kc, ks, vc, vs = _qkv_outputs(T, H, d, xc.device)
+    dev = _on_one_gpu(((xc, "xc"), (xs, "xs")))
+    _u8_operand(xc, "xc", T * (C // 2))
+    _u8_operand(xs, "xs", T * (C // 32))
+    _gemm_weights(wc, ws, 3 * H * d, C, dev)
+    q, kc, ks, vc, vs = _qkv_outputs(T, H, d, dev)
     _check(lib().mxqkv_proj_quantized(xc.data_ptr(), xs.data_ptr(), wc.data_ptr(), ws.data_ptr(), T, C, H, d,
                                       _mode(mode), q.data_ptr(), kc.data_ptr(), ks.data_ptr(), vc.data_ptr(),
                                       vs.data_ptr(), _stream(xc)), "mxqkv_proj_quantized")
@@ -339,13 +456,14 @@ def qkv_proj_quantized(xc, xs, wc, ws, T: int, C: int, H: int, d: int, mode="uos
 def qkv_proj(x, wc, ws, H: int, d: int, mode="uos", workspace=None):
     """mxqkv_proj on bf16 x [T, C] (W quantized beforehand with quantize(...,
     axis=1) as [3*H*d, C]); returns (q, kc, ks, vc, vs) as qkv_proj_quantized."""
-    import torch
+    dev = _on_one_gpu(((x, "x"),))
     x = _bf16_device(x, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be a bf16 [T, C] tensor")
     T, C = x.shape
-    q, kc, ks, vc, vs = _qkv_outputs(T, H, d, x.device)
-    need = int(lib().mxgemm_workspace_bytes(T, C))
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _gemm_weights(wc, ws, 3 * H * d, C, dev)
+    q, kc, ks, vc, vs = _qkv_outputs(T, H, d, dev)
+    workspace = _workspace(workspace, int(lib().mxgemm_workspace_bytes(T, C)), dev)
     _check(lib().mxqkv_proj(x.data_ptr(), wc.data_ptr(), ws.data_ptr(), T, C, H, d, _mode(mode), q.data_ptr(),
                             kc.data_ptr(), ks.data_ptr(), vc.data_ptr(), vs.data_ptr(), workspace.data_ptr(),
                             workspace.numel(), _stream(x)), "mxqkv_proj")
@@ -353,8 +471,17 @@ def qkv_proj(x, wc, ws, H: int, d: int, mode="uos", workspace=None):
 
 
 def dump(path: str, codes, scales, batch: int, nvec: int, L: int, axis: int, mode="uos") -> None:
-    """Write (codes, scales) in the "MXQ1" reference format (synchronous)."""
+    """Write (codes, scales) in the "MXQ1" reference format (synchronous).
+    codes and scales are both CUDA tensors or both host tensors."""
     import torch
-    stream = _stream(codes) if isinstance(codes, torch.Tensor) and codes.is_cuda else None
+    for t, n in ((codes, "codes"), (scales, "scales")):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.uint8 or not t.is_contiguous():
+            raise TypeError(f"{n} must be a contiguous uint8 tensor")
+    if codes.device != scales.device:
+        raise ValueError(f"codes ({codes.device}) and scales ({scales.device}) must be in the same memory")
+    nb = n_blocks(L)
+    _u8_operand(codes, "codes", batch * nvec * nb * 16)
+    _u8_operand(scales, "scales", batch * nvec * nb)
+    stream = _stream(codes) if codes.is_cuda else None
     _check(lib().mxq_dump(path.encode(), codes.data_ptr(), scales.data_ptr(), batch, nvec, L,
                           int(axis), _mode(mode), stream), "mxq_dump")

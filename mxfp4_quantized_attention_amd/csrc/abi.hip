@@ -42,6 +42,7 @@ namespace {
 constexpr int64_t kMaxElems = int64_t(1) << 40;  // per quantize call
 constexpr int64_t kMaxAttnElems = int64_t(1) << 34;  // B*H*N*d per attention call
 constexpr int kKvTile = 128;
+constexpr int64_t kQueryTile = 128;  // queries per attention workgroup (kBR in attention.hip)
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool valid_mode(int mode) { return mode == MXQ_MODE_OCP || mode == MXQ_MODE_UOS; }
@@ -74,8 +75,8 @@ int check_attn_sizes(int64_t B, int64_t H, int64_t N, int64_t d) {
   if (B > (int64_t(1) << 20) || H > (int64_t(1) << 20) || N > (int64_t(1) << 24)) return MXQ_ERR_UNSUPPORTED;
   const int64_t BH = B * H;
   if (BH > (int64_t(1) << 24) || BH * N * d > kMaxAttnElems) return MXQ_ERR_UNSUPPORTED;
-  // the workgroup count (BH * ceil(N / 256), rounded to 8) must fit an int
-  if (BH * ((N + 255) / 256) + 8 > (int64_t(1) << 31) - 1) return MXQ_ERR_UNSUPPORTED;
+  // the workgroup count (BH * ceil(N / kQueryTile), rounded up to 8) must fit an int
+  if (BH * ((N + kQueryTile - 1) / kQueryTile) + 8 > (int64_t(1) << 31) - 1) return MXQ_ERR_UNSUPPORTED;
   return MXQ_OK;
 }
 
@@ -113,7 +114,7 @@ int check_varlen_sizes(int64_t batch, int64_t T, int64_t H, int64_t d) {
   const int64_t vstride = (T + 31) / 32 + batch;
   if (d * vstride * 16 > (int64_t(1) << 31) - 1) return MXQ_ERR_UNSUPPORTED;
   if (H * T * d > kMaxAttnElems) return MXQ_ERR_UNSUPPORTED;
-  if (H * ((T + 127) / 128 + batch) + 8 > (int64_t(1) << 31) - 1) return MXQ_ERR_UNSUPPORTED;
+  if (H * ((T + kQueryTile - 1) / kQueryTile + batch) + 8 > (int64_t(1) << 31) - 1) return MXQ_ERR_UNSUPPORTED;
   return MXQ_OK;
 }
 
@@ -412,17 +413,21 @@ int mxq_dump(const char* path, const uint8_t* codes, const uint8_t* scales, int6
   hdr[255] = '\n';
 
   // Device pointers are copied on the caller's stream; host memory (or any
-  // pointer the runtime does not know) is read directly.
+  // pointer the runtime does not know) is read directly.  codes and scales
+  // must live in the same kind of memory: a device/host mix is rejected.
   std::vector<uint8_t> hc, hs;
   const uint8_t* pc = codes;
   const uint8_t* ps = scales;
   if (ncode > 0) {
-    hipPointerAttribute_t attr;
-    bool on_device = false;
-    if (hipPointerGetAttributes(&attr, codes) == hipSuccess)
-      on_device = attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged;
-    else
-      (void)hipGetLastError();  // unknown pointer: treat as host memory
+    auto device_memory = [](const void* p) {
+      hipPointerAttribute_t attr;
+      if (hipPointerGetAttributes(&attr, p) == hipSuccess)
+        return attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged;
+      (void)hipGetLastError();  // unknown pointer: host memory
+      return false;
+    };
+    const bool on_device = device_memory(codes);
+    if (device_memory(scales) != on_device) return MXQ_ERR_INVALID_ARG;
     if (on_device) {
       hc.resize(ncode);
       hs.resize(nscale);

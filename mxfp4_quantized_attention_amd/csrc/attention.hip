@@ -213,7 +213,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   // on one XCD stream the same head's K/V through that XCD's L2.
   const int w = blockIdx.x;
   const int lin = (w & 7) * a.per_xcd + (w >> 3);
-  if (lin >= a.BH * a.ntq) return;
+  if (lin >= int64_t(a.BH) * a.ntq) return;
   const int64_t bh = lin / a.ntq;  // dense: batch * H + head; varlen: head
   int qt = lin % a.ntq;
   int N = a.N;
@@ -525,8 +525,8 @@ void launch_variant(const AttnArgs& a, dim3 grid, bool qbf16, bool varlen, hipSt
 }
 
 hipError_t launch(AttnArgs& a, int d, int mode, bool pnq, bool varlen, float softmax_scale, hipStream_t stream) {
-  const int total = a.BH * a.ntq;
-  a.per_xcd = (total + 7) / 8;
+  const int64_t total = int64_t(a.BH) * a.ntq;  // fits an int: the ABI checks it
+  a.per_xcd = int((total + 7) / 8);
   a.c = softmax_scale * 1.4426950408889634f;
   const dim3 grid(unsigned(a.per_xcd * 8));
   const bool qbf16 = a.q != nullptr;

@@ -25,27 +25,41 @@ MODE_NONE = 2  # identity quantizer, pins only
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "mxoracle.c")
 _LIB = os.path.join(_HERE, "libmxoracle.so")
+# An alternative build of the same source (the sanitizer test points this at
+# an AddressSanitizer/UBSan build); the default is the library build() makes.
+_LIB_OVERRIDE = os.environ.get("MXORACLE_LIB")
 _lib = None
 
 
-def build(force: bool = True) -> str:
-    """Compile the oracle with gcc (strict IEEE: no fast-math, no FMA contraction)."""
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp%d" % os.getpid()
-        cmd = ["gcc", "-O2", "-std=c99", "-D_GNU_SOURCE", "-fopenmp", "-ffp-contract=off",
-               "-Wall", "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"]
+GCC_FLAGS = ["-std=c99", "-D_GNU_SOURCE", "-fopenmp", "-ffp-contract=off", "-Wall", "-shared", "-fPIC"]
+SANITIZE_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                  "-fno-sanitize-recover=all"]
+
+
+def build(force: bool = True, out: str | None = None, sanitize: bool = False) -> str:
+    """Compile the oracle with gcc (strict IEEE: no fast-math, no FMA
+    contraction).  sanitize=True builds the same source with AddressSanitizer
+    and UBSan (every report fatal) into `out` instead, for the sanitizer test."""
+    target = out or _LIB
+    if force or not os.path.exists(target):
+        tmp = target + ".tmp%d" % os.getpid()
+        opt = SANITIZE_FLAGS if sanitize else ["-O2"]
+        cmd = ["gcc", *opt, *GCC_FLAGS, _SRC, "-o", tmp, "-lm"]
         subprocess.run(cmd, check=True)
-        os.replace(tmp, _LIB)
-    return _LIB
+        os.replace(tmp, target)
+    return target
 
 
 def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB):
-        build(force=True)
-    lib = ctypes.CDLL(_LIB)
+    if _LIB_OVERRIDE:
+        lib = ctypes.CDLL(_LIB_OVERRIDE)
+    else:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
     P = ctypes.c_void_p
     i64 = ctypes.c_int64
     i32 = ctypes.c_int

@@ -38,6 +38,26 @@ def test_bnhd_equals_dense(B, H, N, d, mode, pnq):
     assert same_bits(o, ref)
 
 
+@pytest.mark.parametrize("B,H,N,d,mode,pnq", [(2, 3, 1000, 128, "uos", True), (1, 4, 513, 64, "ocp", False),
+                                              (1, 2, 4096, 128, "uos", True)])
+def test_bnhd_against_oracle(B, H, N, d, mode, pnq):
+    """mxattn_fwd_strided on [B, N, H, d] tensors compared with the oracle
+    directly (not only with the dense entry point)."""
+    import oracle
+    from gpu_helpers import compare_attention, to_np_u16
+    g = np.random.default_rng(B * 100 + H * 10 + N + d)
+    bnhd = [workloads.f32_to_bf16((g.standard_normal((B, N, H, d)) * 1.5).astype(np.float32)) for _ in range(3)]
+    q, k, v = (torch.from_numpy(x.view(np.int16)).to("cuda:0").view(torch.bfloat16).transpose(1, 2) for x in bnhd)
+    o = mx.fwd_strided(q, k, v, mode=mode, pnq=pnq)
+    torch.cuda.synchronize()
+    got = to_np_u16(o).reshape(B * H * N, d)  # .contiguous() gives [B][H][N][d] order
+    bhnd = [np.ascontiguousarray(x.transpose(0, 2, 1, 3)) for x in bnhd]
+    omode = oracle.MODE_UOS if mode == "uos" else oracle.MODE_OCP
+    rows = np.arange(B * H * N) if B * H * N <= 8192 else workloads.sample_rows(B * H, N, 1024)
+    ref = oracle.attn_rows(*bhnd, B * H, N, d, omode, pnq, mx.kv_tile(d), 1 / np.sqrt(d), rows)
+    compare_attention(got[rows], ref, what=f"BNHD {(B, N, H, d)} {mode} pnq={pnq}")
+
+
 @pytest.mark.parametrize("B,H,N,d", SHAPES[:2])
 def test_packed_qkv_slices(B, H, N, d):
     qkv = rand_bf16((B, N, 3, H, d), seed=5)

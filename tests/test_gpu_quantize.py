@@ -88,6 +88,39 @@ def test_ragged_shapes(shape, omode, gmode):
     check(x, 0, omode, gmode, f"{shape} axis 0")
 
 
+@pytest.mark.parametrize("shape", [(3, 1000, 700), (1, 2049, 1030), (2, 300, 257), (1, 64, 4096)])
+@pytest.mark.parametrize("omode,gmode", MODES)
+def test_axis0_wide_ragged(shape, omode, gmode):
+    """Blocks along rows for inputs wider than one 64-column tile: every
+    column tile (the ragged last one too) and every row tile, bit for bit."""
+    g = np.random.default_rng(sum(shape) + 7)
+    x = workloads.f32_to_bf16((g.standard_normal(shape) * np.exp2(g.uniform(-20, 20, shape))).astype(np.float32))
+    check(x, 0, omode, gmode, f"{shape} axis 0")
+
+
+def test_sweep_axis0_sampled():
+    """The sweep's row-axis case, 2^28 values viewed [2^18, 1024] with blocks
+    along rows (the configuration the bench times), on 8192 seeded sampled
+    (column, block) pairs per mode, every column tile represented."""
+    R, C = 1 << 18, 1024
+    x = workloads.sweep(28).reshape(R, C)
+    xg = to_gpu_bf16(x.reshape(1, R, C))
+    g = np.random.default_rng(2028)
+    nb = R // 32
+    cols = np.concatenate([np.arange(C), g.integers(0, C, 8192 - C)])
+    blks = np.concatenate([g.integers(0, nb, C - 2), [0, nb - 1], g.integers(0, nb, 8192 - C)])
+    sub = np.stack([x[32 * b: 32 * b + 32, c] for c, b in zip(cols, blks)])
+    flat = torch_index(cols.astype(np.int64) * nb + blks)
+    for omode, gmode in MODES:
+        c, s = mx.quantize(xg, mode=gmode, axis=0)
+        cg = c.view(-1, 16)[flat].cpu().numpy().reshape(-1)
+        sg = s.view(-1)[flat].cpu().numpy()
+        ec, es = oracle.quantize_bf16(sub, 1, sub.shape[0], 32, 1, omode)
+        np.testing.assert_array_equal(sg, es)
+        np.testing.assert_array_equal(cg, ec)
+        del c, s
+
+
 @pytest.mark.parametrize("p", [20, 22, 24])
 @pytest.mark.parametrize("omode,gmode", MODES)
 def test_sweep_full(p, omode, gmode):
