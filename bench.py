@@ -51,14 +51,14 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_wan_traffic.json")
 GEMM_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_dit_ffn_traffic.json")
 UTIL_FILE = os.path.join(ROOT, "profiles", "attn_fwd_wan_utilization.json")
-# The vector-unit ceiling of the attention kernel.  Every score element needs
-# one fma (scale and max shift), one exponential, half a three-input max and
-# half a two-element FP4 convert.  Measured gfx950 issue costs, in units of one
-# wave64 v_fma_f32 (1.13 ns of a SIMD): exp 3.2, FP4 convert 4.1 per two
-# elements, max3 1.6 per two elements; 1024 SIMDs.
-VALU_SLOTS_PER_SCORE = 1.0 + 3.2 + 4.1 / 2 + 1.6 / 2
-VALU_SLOT_NS = 1.13
+# The vector-unit ceiling of the attention kernel comes from the committed
+# instruction-cost probe (bench.py --workload valu_probe, probe.hip): every
+# score element needs one fma (scale and max shift), one exponential, half a
+# three-input max and half a two-element FP4 convert, and every 2048 scores of
+# a wave's key tile take 17 scaled FP4 MFMAs at d = 128 (8 for S, 8 for P.V,
+# 1 for the PNQ row sum; 13 at d = 64).  1024 SIMDs.
 N_SIMDS = 1024
+PROBE_FILE = os.path.join(ROOT, "profiles", "attn_valu_probe.json")
 ATTN_SRC = os.path.join(ROOT, "mxfp4_quantized_attention_amd", "csrc", "attention.hip")
 
 
@@ -117,11 +117,29 @@ def copy_calibration(mib: int, dev) -> None:
     del src, dst
 
 
-def valu_ceiling_tflops(d: int) -> float:
+def measured_probe():
+    """The committed instruction-cost probe summary, or None when it was taken
+    on another version of the probe kernel."""
+    try:
+        with open(PROBE_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("probe_sha") != source_hash("probe.hip"):
+        return None
+    return t
+
+
+def valu_ceilings(d: int, probe: dict, clock_ghz: float) -> dict:
     """FLOP/s (4 d per score element) at which the per-score vector work alone
-    would fill every SIMD's issue slots."""
-    scores_per_s = N_SIMDS * 64 / (VALU_SLOTS_PER_SCORE * VALU_SLOT_NS * 1e-9)
-    return 4.0 * d * scores_per_s / 1e12
+    fills every SIMD's issue cycles (MFMA entirely hidden), and with the MFMAs
+    serialized behind it, from the probe's cycle costs at `clock_ghz`."""
+    cyc = {k: v * probe["clock_ghz"] for k, v in probe["ns_per_wave_instruction"].items()}
+    valu = (cyc["fma"] + cyc["exp"] + cyc["cvt"] / 2 + cyc["max3"] / 2) / 64.0  # SIMD cycles per score
+    mfma = (17.0 if d == 128 else 13.0) * cyc["mfma"] / 2048.0
+    per = lambda c: 4.0 * d * N_SIMDS * clock_ghz * 1e9 / c / 1e12
+    return {"valu_cycles_per_score": valu, "mfma_cycles_per_score": mfma,
+            "ceiling": per(valu), "ceiling_mfma_serialized": per(valu + mfma)}
 
 
 def measured_utilization(workload: str):
@@ -139,13 +157,21 @@ def measured_utilization(workload: str):
 
 
 def valu_bound(achieved: float, d: int, workload: str) -> dict:
-    ceiling = valu_ceiling_tflops(d)
+    probe = measured_probe()
     util = measured_utilization(workload)
-    return {"bound": "valu", "ceiling": ceiling, "unit": "TFLOP/s", "frac": achieved / ceiling,
-            "slots_per_score": VALU_SLOTS_PER_SCORE, "slot_ns": VALU_SLOT_NS,
-            "valu_active": util["valu_active"] if util else None,
-            "mfma_busy": util["mfma_busy"] if util else None,
-            "clock_ghz_profiled": util["clock_ghz"] if util else None}
+    out = {"bound": "valu", "unit": "TFLOP/s", "source": "profiles/attn_valu_probe.json",
+           "valu_active": util["valu_active"] if util else None,
+           "mfma_busy": util["mfma_busy"] if util else None,
+           "clock_ghz_profiled": util["clock_ghz"] if util else None}
+    if probe is None:
+        out.update(ceiling=None, frac=None, note="probe summary missing or taken on another probe version")
+        return out
+    clock = util["clock_ghz"] if util else probe["clock_ghz"]
+    c = valu_ceilings(d, probe, clock)
+    out.update(c)
+    out.update(frac=achieved / c["ceiling"], clock_ghz_used=clock, clock_ghz_probe=probe["clock_ghz"],
+               slots_per_score=probe["slots_per_score"], probe_sha=probe["probe_sha"])
+    return out
 
 
 def cpu_model() -> str:
@@ -250,7 +276,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="wan", choices=["tiny", "small", "wan", "hunyuan", "sweep", "gemm", "wan_varlen", "wan_block"])
+    ap.add_argument("--workload", default="wan", choices=["tiny", "small", "wan", "hunyuan", "sweep", "gemm", "wan_varlen",
+                                                          "wan_block", "valu_probe"])
+    ap.add_argument("--probe-out", default="", help="valu_probe: also write the summary JSON here")
     ap.add_argument("--mode", default="uos", choices=["uos", "ocp"])
     ap.add_argument("--no-pnq", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -285,6 +313,9 @@ def main():
         return
     if args.workload == "wan_block":
         block_bench(args, dev)
+        return
+    if args.workload == "valu_probe":
+        probe_bench(args, dev)
         return
     cfg = workloads.CONFIGS[args.workload]
     B, H, N, d = cfg["B"], cfg["H"], cfg["N"], cfg["d"]
@@ -407,6 +438,94 @@ def main():
         result["cpu_baseline"] = cpu_baseline(q, k, v, args.workload, mode, pnq, mx.kv_tile(d), gpu_out,
                                               **({"heads": B * H, "rows_per_head": N} if full else {}))
     print(json.dumps(result), flush=True)
+
+
+PROBE_OPS = {"fma": 1, "exp": 2, "cvt": 3, "max3": 4, "mfma": 5}
+
+
+def probe_bench(args, dev):
+    """Issue costs of the attention kernel's per-score instructions and their
+    overlap with the scaled FP4 MFMA (libmxprobe.so; see probe.hip).  Prints one
+    JSON line; --probe-out also writes it as the summary valu_bound reads."""
+    import ctypes
+    import numpy as np
+    import torch
+    from mxfp4_quantized_attention_amd import build as hip_build
+
+    P = ctypes.CDLL(hip_build.PROBE_LIB)
+    i32 = ctypes.c_int
+    P.mxprobe_launch.argtypes = [i32, i32, i32, i32, i32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    P.mxprobe_launch.restype = i32
+    wg = 4  # workgroups per CU: 4 waves of each role per SIMD
+    out = torch.zeros(256 * wg * 8, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(2, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def run(op_a, it_a, op_b=0, it_b=0, reps=5):
+        times = []
+        for r in range(reps + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            st = P.mxprobe_launch(op_a, it_a, op_b, it_b, wg, out.data_ptr(), clocks.data_ptr(), stream.cuda_stream)
+            e1.record(stream)
+            if st != 0:
+                raise RuntimeError(f"probe launch failed ({st})")
+            torch.cuda.synchronize()
+            if r:
+                times.append(e0.elapsed_time(e1))
+        return float(np.median(times))
+
+    target_ms = 3.0
+
+    def iters_for(op, it0=512):
+        t = run(op, it0, reps=2)
+        return max(64, int(it0 * target_ms / max(t, 1e-3)))
+
+    log("[probe] costs of each instruction alone (4 waves per SIMD)")
+    cost, iters = {}, {}
+    for name, op in PROBE_OPS.items():
+        iters[name] = iters_for(op)
+        t = run(op, iters[name])
+        cost[name] = t * 1e6 / (wg * iters[name] * 8)  # ns per wave instruction per SIMD
+        log(f"[probe] {name}: {cost[name]:.3f} ns")
+    ghz = float(clocks[0].item()) / (float(clocks[1].item()) * 10.0)
+    slot = cost["fma"]
+    log("[probe] overlap with the scaled FP4 MFMA on other waves of the same SIMD")
+    overlap = {}
+    for name in ("fma", "exp", "cvt", "max3"):
+        ta = run(PROBE_OPS[name], iters[name])
+        tb = run(0, 0, PROBE_OPS["mfma"], iters["mfma"])
+        tab = run(PROBE_OPS[name], iters[name], PROBE_OPS["mfma"], iters["mfma"])
+        overlap[name] = (ta + tb - tab) / min(ta, tb)
+        log(f"[probe] {name} + mfma: alone {ta:.3f} / {tb:.3f} ms, together {tab:.3f} ms, overlap {overlap[name]:.2f}")
+    log("[probe] one MFMA and R vector instructions interleaved in one wave")
+    mixed = {}
+    for name in ("fma", "exp", "cvt", "max3"):
+        for R in (1, 2, 4, 8):
+            op = 16 + 4 * R + (PROBE_OPS[name] & 3)
+            it = max(64, int(target_ms * 1e6 / (wg * 8 * (cost["mfma"] + R * cost[name]))))
+            t = run(op, it)
+            per = t * 1e6 / (wg * it * 8)  # ns per (MFMA + R instructions) per SIMD
+            alone = cost["mfma"] + R * cost[name]
+            hidden = (alone - per) / min(cost["mfma"], R * cost[name])
+            mixed[f"{name}x{R}"] = {"ns": per, "serial_ns": alone, "hidden": hidden}
+            log(f"[probe] mfma + {R} {name}: {per:.2f} ns (serial {alone:.2f}), hidden {hidden:.2f}")
+    slots = (cost["fma"] + cost["exp"] + cost["cvt"] / 2 + cost["max3"] / 2) / slot
+    summary = {
+        "probe": "attention per-score instruction costs, gfx950",
+        "probe_sha": source_hash("probe.hip"),
+        "clock_ghz": ghz,
+        "ns_per_wave_instruction": cost,
+        "slot_ns": slot,
+        "slots": {k: v / slot for k, v in cost.items()},
+        "slots_per_score": slots,
+        "overlap_with_mfma_other_waves": overlap,
+        "mfma_interleaved_same_wave": mixed,
+    }
+    print(json.dumps(summary), flush=True)
+    if args.probe_out:
+        with open(args.probe_out, "w") as f:
+            json.dump(summary, f, indent=1)
 
 
 def gemm_bench(args, dev):

@@ -18,6 +18,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmxattn.so")
 SOURCES = ["abi.hip", "quantize.hip", "attention.hip", "gemm.hip"]
+# The instruction-cost probe behind the attention kernel's vector-unit ceiling
+# (bench.py --workload valu_probe): a library of its own, not part of the path.
+PROBE_SOURCES = ["probe.hip"]
+PROBE_LIB = os.path.join(HERE, "libmxprobe.so")
 # The attention kernel never sees a NaN (inputs are finite by contract and the
 # running max starts at -inf, never inf - inf); without NaNs the compiler drops
 # the canonicalizing moves it otherwise puts in front of every fmaxf.
@@ -54,16 +58,21 @@ def build(verbose: bool = False) -> str:
             print(msgs)
         return obj
 
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+    with ThreadPoolExecutor(max_workers=len(SOURCES) + len(PROBE_SOURCES)) as ex:
+        objs = list(ex.map(compile_one, SOURCES + PROBE_SOURCES))
+    link(objs[:len(SOURCES)], LIB)
+    link(objs[len(SOURCES):], PROBE_LIB)
+    build_abi_demo(objdir)
+    return LIB
+
+
+def link(objs, out):
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-fno-gpu-rdc", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
-    build_abi_demo(objdir)
-    return LIB
+    os.replace(tmp, out)
 
 
 DEMO_SRC = os.path.join(ROOT, "tests", "abi_demo.c")

@@ -51,12 +51,12 @@ def attention_tolerance(ref, atol=2e-3):
     return r, tol
 
 
-def compare_attention(gpu_bits, ref, atol=2e-3, rel_l2_max=1e-3, what="", require_no_budget=False):
+def compare_attention(gpu_bits, ref, atol=2e-3, rel_l2_max=1e-3, what="", max_budget_rows=None):
     """Acceptance for the bf16 attention output against the oracle: every
     element within attention_tolerance, and relative L2 <= rel_l2_max over all
-    checked elements.  require_no_budget: every element must also meet the
-    base bound max(atol, 1 bf16 ulp) on its own, i.e. no row may lean on the
-    flip budget of its near-tie decisions."""
+    checked elements.  max_budget_rows: at most this many rows may have an
+    element beyond the base bound max(atol, 1 bf16 ulp), i.e. lean on the flip
+    budget of their near-tie decisions (0: none may)."""
     r, tol = attention_tolerance(ref, atol)
     g = oracle.bf16_to_f64(gpu_bits).reshape(r.shape)
     diff = np.abs(g - r)
@@ -70,6 +70,6 @@ def compare_attention(gpu_bits, ref, atol=2e-3, rel_l2_max=1e-3, what="", requir
     print(what, info)
     assert not bad.any(), f"{what}: elements beyond tolerance: {info}"
     assert rel <= rel_l2_max, f"{what}: relative L2 {rel} > {rel_l2_max}"
-    if require_no_budget:
-        assert info["rows_using_budget"] == 0, f"{what}: rows needing their flip budget: {info}"
+    if max_budget_rows is not None:
+        assert info["rows_using_budget"] <= max_budget_rows, f"{what}: rows needing their flip budget: {info}"
     return info
