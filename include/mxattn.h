@@ -143,6 +143,27 @@ int mxattn_fwd(const void *q, const void *k, const void *v, int64_t B, int64_t H
                size_t workspace_bytes, void *stream);
 
 /*
+ * mxattn_fwd_noalloc -- mxattn_fwd without a workspace argument, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  The quantized K and V go
+ * to a device array inside the library (mxattn_noalloc_max_bytes() = 256 MiB,
+ * one copy per GPU, held until the process ends) instead of a workspace; the
+ * call allocates nothing.  Arguments, kernels and results are those of
+ * mxattn_fwd (bit-identical).  The array's address is looked up on the first
+ * call on each device, with the caller's current device, which must be the
+ * device of `stream` and of the tensors.  Every call on one GPU uses that
+ * GPU's one array: calls that overlap in time on one GPU race, so callers
+ * order them (one stream, or synchronization between streams).
+ * Errors as mxattn_fwd; MXQ_ERR_WORKSPACE when mxattn_workspace_bytes(B, H,
+ * N, d) exceeds mxattn_noalloc_max_bytes().
+ */
+int mxattn_fwd_noalloc(const void *q, const void *k, const void *v, int64_t B, int64_t H, int64_t N,
+                       int64_t d, int mode, int pnq, float softmax_scale, void *o, void *stream);
+
+/* Size in bytes of mxattn_fwd_noalloc's device array (its largest workspace). */
+size_t mxattn_noalloc_max_bytes(void);
+
+/*
  * mxattn_fwd_quantized -- the fused kernel alone, on operands already in the
  * canonical layouts of mxq_quantize (batch = B*H):
  *   qc, kc: [B*H][N][d/2], qs, ks: [B*H][N][d/32]   (axis 1, rows = N, cols = d)

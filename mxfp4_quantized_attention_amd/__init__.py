@@ -76,6 +76,10 @@ def lib() -> ctypes.CDLL:
     L.mxqkv_proj_quantized.restype = i32
     L.mxqkv_proj.argtypes = [P, P, P, i64, i64, i64, i64, i32, P, P, P, P, P, P, ctypes.c_size_t, P]
     L.mxqkv_proj.restype = i32
+    L.mxattn_fwd_noalloc.argtypes = [P, P, P, i64, i64, i64, i64, i32, i32, f32, P, P]
+    L.mxattn_fwd_noalloc.restype = i32
+    L.mxattn_noalloc_max_bytes.argtypes = []
+    L.mxattn_noalloc_max_bytes.restype = ctypes.c_size_t
     _lib = L
     return L
 
@@ -84,7 +88,7 @@ EXPORTS = ("mxq_status_string", "mxattn_version", "mxq_quantize", "mxattn_kv_til
            "mxattn_workspace_bytes", "mxattn_fwd", "mxattn_fwd_quantized", "mxattn_fwd_kv_quantized",
            "mxgemm_quantized", "mxgemm_workspace_bytes", "mxgemm", "mxattn_fwd_strided",
            "mxq_quantize_strided", "mxq_dump", "mxattn_varlen_workspace_bytes", "mxattn_fwd_varlen",
-           "mxqkv_proj_quantized", "mxqkv_proj")
+           "mxqkv_proj_quantized", "mxqkv_proj", "mxattn_fwd_noalloc", "mxattn_noalloc_max_bytes")
 
 
 def status_string(status: int) -> str:
@@ -253,6 +257,24 @@ def fwd(q, k, v, mode="uos", pnq: bool = True, softmax_scale: float = 0.0, works
     _check(lib().mxattn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, N, d, _mode(mode),
                             int(bool(pnq)), float(softmax_scale), o.data_ptr(), workspace.data_ptr(),
                             workspace.numel(), _stream(q)), "mxattn_fwd")
+    return o
+
+
+def noalloc_max_bytes() -> int:
+    return int(lib().mxattn_noalloc_max_bytes())
+
+
+def fwd_noalloc(q, k, v, mode="uos", pnq: bool = True, softmax_scale: float = 0.0, out=None):
+    """``fwd`` without a workspace: the quantized K and V live in the library's
+    own device array (mxattn_fwd_noalloc; the call allocates nothing when
+    `out` is given).  Calls on one GPU share that array, so they must not
+    overlap in time."""
+    import torch
+    B, H, N, d, dev = _qkv4(q, k, v)
+    o = torch.empty_like(q) if out is None else _check_out(out, q.shape, dev)
+    _check(lib().mxattn_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, N, d, _mode(mode),
+                                    int(bool(pnq)), float(softmax_scale), o.data_ptr(), _stream(q)),
+           "mxattn_fwd_noalloc")
     return o
 
 

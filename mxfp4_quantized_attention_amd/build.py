@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmxattn.so")
-SOURCES = ["abi.hip", "quantize.hip", "attention.hip", "gemm.hip"]
+SOURCES = ["abi.hip", "quantize.hip", "attention.hip", "gemm.hip", "noalloc.hip"]
 # The instruction-cost probe behind the attention kernel's vector-unit ceiling
 # (bench.py --workload valu_probe): a library of its own, not part of the path.
 PROBE_SOURCES = ["probe.hip"]
