@@ -136,9 +136,10 @@ struct __align__(16) TileLds {
 
 // Online-softmax step for one 16-query group on one key tile: running max,
 // exponentials, block scales and the packed FP4 operand.  S holds this lane's
-// 32 scores (query r16, keys 32*g4 + 4t + jj).
+// 32 scores (query r16, keys 32*g4 + 4t + jj).  Returns whether any running
+// max of the wave moved (alpha is then exp2((m_old - m_new) c), else 1).
 template <int MODE, bool PNQ>
-__device__ __forceinline__ void softmax_group(v4f (&S)[8], float& m, float c, uint4& pk, int& pS,
+__device__ __forceinline__ bool softmax_group(v4f (&S)[8], float& m, float c, uint4& pk, int& pS,
                                               float& alpha, float& lpart) {
   // two independent chains of three-input maxima over the 32 scores
   float b0 = fmaxf(fmaxf(S[0][0], S[0][1]), S[0][2]);
@@ -153,17 +154,30 @@ __device__ __forceinline__ void softmax_group(v4f (&S)[8], float& m, float c, ui
   }
   const float bm = fmaxf(b0, b1);
   const float rm = max_over_blocks(bm);
-  const float mnew = fmaxf(m, rm);
-  alpha = fast_exp2((m - mnew) * c);
+  const float mold = m;
+  const float mnew = fmaxf(mold, rm);
+  const bool moved = __any(mnew != mold);
+  alpha = 1.0f;
+  if (moved) alpha = fast_exp2((mold - mnew) * c);
   m = mnew;
   const float mc = mnew * c;
-  // block scale from the block max; (bm - mnew) is exactly 0 in the block
-  // holding the row max, so that block's amax is exactly 1
-  const float amax = fast_exp2((bm - mnew) * c);
-  int e = block_exp_f32bits<MODE>(__float_as_uint(amax));
-  e = e < -126 ? -126 : e;
-  pS = e + 127;
-  const float sc = pow2f(e);
+  // Block exponent from xb = log2 of the block's largest exponential,
+  // (bm - m) c, which is exactly 0 in the block holding the running max (its
+  // amax is exactly 1).  OCP: e = floor(xb) - 2.  UOS: the least e with
+  // 2^xb <= 7.25 2^e, e = ceil(xb - log2 7.25) = -floor(log2 7.25 - xb).
+  // Both clamp at -126 (the convert takes its scale as a normal fp32); a block
+  // with no valid key has xb = -inf and lands on the clamp.
+  const float xb = (bm - mnew) * c;
+  int eb;  // e + 127
+  if (MODE == kModeUOS) {
+    const int f = int(floorf(2.857981f - xb));  // log2(7.25)
+    eb = 127 - min(f, 126);
+  } else {
+    const int f = int(floorf(xb));
+    eb = max(f, -124) + 125;
+  }
+  pS = eb;
+  const float sc = __uint_as_float(uint32_t(eb) << 23);
   // exponentials and their FP4 codes, one 8-code dword at a time (nibble n
   // of the operand = key 32*g4 + n, n = 4t + jj)
   uint32_t d[4];
@@ -190,6 +204,7 @@ __device__ __forceinline__ void softmax_group(v4f (&S)[8], float& m, float c, ui
   }
   pk = make_uint4(d[0], d[1], d[2], d[3]);
   if (!PNQ) lpart = lpart * alpha + ps;
+  return moved;
 }
 
 }  // namespace
@@ -437,9 +452,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
       // the VALU-heavy part of the tile runs at raised wave priority, so a
       // SIMD prefers issuing it over waves that sit in their MFMA phases
       __builtin_amdgcn_s_setprio(1);
-      softmax_group<MODE, PNQ>(S[g], m[g], c, pk[g], pS[g], alpha, lpart[g]);
+      const bool moved = softmax_group<MODE, PNQ>(S[g], m[g], c, pk[g], pS[g], alpha, lpart[g]);
       __builtin_amdgcn_s_setprio(0);
-      if (__any(alpha != 1.0f)) {  // rescale only when some running max moved
+      if (moved) {  // rescale only when some running max moved
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) O[g][ct] *= alpha;
         if (PNQ) L[g][0] *= alpha;  // the four entries are equal; only [0] is read
@@ -465,6 +480,13 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
     // barrier, and the wait for the next tile's fills comes mid-tile.
 #pragma unroll
     for (int g = 0; g < kQG; ++g) asm volatile("" ::"v"(pk[g].x), "v"(pk[g].y), "v"(pk[g].z), "v"(pk[g].w));
+    // The same for the P.V MFMAs: kept above the barrier, their V operands
+    // are read and consumed inside the tile instead of living across the
+    // barrier next to the next tile's scores (100 VGPRs instead of 108).
+#pragma unroll
+    for (int g = 0; g < kQG; ++g)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) asm volatile("" : "+v"(O[g][ct]));
   };
 
   // ---- tile loop over two LDS buffers ----

@@ -16,23 +16,11 @@ enum : int { kModeOCP = 0, kModeUOS = 1 };
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-// Block exponent from the bit pattern of a non-negative fp32 amax.
-// amax = 2^E * M, M in [1, 2): OCP e = E - 2; UOS e = E - 2 + [M > 1.8125],
-// which is the least e with amax <= 7.25 * 2^e (7.25 = 1.8125 * 4).  1.8125
-// is mantissa field 0x680000.  A zero or subnormal amax has exponent field 0
-// and lands below -127, where the clamp puts it.
-template <int MODE>
-__device__ __forceinline__ int block_exp_f32bits(uint32_t bits) {
-  int E = int((bits >> 23) & 0xFFu) - 127;
-  int e = E - 2;
-  if (MODE == kModeUOS) e += (bits & 0x7FFFFFu) > 0x680000u ? 1 : 0;
-  e = e < -127 ? -127 : e;
-  e = e > 127 ? 127 : e;
-  return e;
-}
-
-// Same rule from the bit pattern of a non-negative bf16 amax (7 mantissa bits;
-// 1.8125 is mantissa field 0x68).
+// Block exponent from the bit pattern of a non-negative bf16 amax.  amax =
+// 2^E * M, M in [1, 2): OCP e = E - 2; UOS e = E - 2 + [M > 1.8125], which is
+// the least e with amax <= 7.25 * 2^e (7.25 = 1.8125 * 4; 1.8125 is mantissa
+// field 0x68 of the 7 bf16 mantissa bits).  A zero or subnormal amax has
+// exponent field 0 and lands below -127, where the clamp puts it.
 template <int MODE>
 __device__ __forceinline__ int block_exp_bf16bits(uint32_t bits) {
   int E = int((bits >> 7) & 0xFFu) - 127;

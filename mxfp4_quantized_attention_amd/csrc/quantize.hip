@@ -148,32 +148,39 @@ struct RowSegments {
   int n;
 };
 
-// Blocks along rows (axis 0).  Work item = a 256-row x 64-column bf16 tile
-// of one batch entry; each workgroup walks items with a grid stride and
-// holds the next item's loads in registers while it encodes the current one
-// from LDS.  Element (row r, column c) of a tile sits at
-// tile[r * 64 + (c ^ 8 (r / 32))], so the eight lanes that read one column
-// of eight 32-row blocks hit eight different banks; eight consecutive lanes
-// take the eight blocks of one column, so a wave writes whole 128-byte code
-// lines.  Rows past the end are zero (padding).
+// Blocks along rows (axis 0).  Work item = a 256-row x TC-column bf16 tile of
+// one batch entry (TC = 128, or 64 for inputs at most 64 columns wide); each
+// workgroup walks items with a grid stride and holds the next item's loads in
+// registers while it encodes the current one from LDS.  Element (row r,
+// column c) of a tile sits at tile[r * TC + (c ^ 8 (r / 32))], so the eight
+// lanes that read one column of eight 32-row blocks hit eight different
+// banks; eight consecutive lanes take the eight blocks of one column, so a
+// wave writes whole 128-byte code lines.  Rows past the end are zero
+// (padding).  Items run row tile first: consecutive items take consecutive
+// 256-row tiles of the same columns, so the code lines the workgroups in
+// flight write are adjacent lines of the same columns.  (Measured on the
+// [2^18][1024] sweep input: 128-column tiles 55% -> 62% of HBM, row-first
+// order 62% -> 63%; the Wan V shape, 128 columns, is unchanged at 63%.)
 //
 // SEG: the rows are the segments of `seg`; ntr is then the number of work
 // tiles per entry (an upper bound on seg.tile[n]: items past it do nothing)
 // and every column holds exactly the blocks of all segments, seg.blk[n]
 // (vstride is ignored).  Otherwise ntr = ceil(rows / 256) and vstride = nb.
-template <int MODE, bool SEG>
+template <int MODE, bool SEG, int TC>
 __global__ __launch_bounds__(256) void quant_cols_kernel(const uint16_t* __restrict__ x,
                                                          uint8_t* __restrict__ codes,
                                                          uint8_t* __restrict__ scales, int64_t rows,
                                                          int64_t cols, int64_t ntr, int64_t ntc,
                                                          int64_t nitems, int64_t vstride, Layout3 in,
                                                          RowSegments seg) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[256 * 64];
+  constexpr int CPR = TC / 8;  // 16-byte chunks per tile row
+  constexpr int LD = CPR;      // chunks loaded per thread (256 rows x CPR chunks / 256 threads)
+  __shared__ __attribute__((aligned(16))) uint16_t tile[256 * TC];
   const int tid = threadIdx.x;
   const bool vec8 = (cols & 7) == 0 && (in.sn & 7) == 0;
   if constexpr (SEG) vstride = seg.blk[seg.n];
   // One work item: entry bi, rows [r0, r0 + nrow) of the input (nrow <= 256),
-  // columns [c0, c0 + 64), output blocks blk0 .. blk0 + nblk - 1.
+  // columns [c0, c0 + TC), output blocks blk0 .. blk0 + nblk - 1.
   struct Item {
     int64_t bi, r0, c0, blk0;
     int nrow, nblk;
@@ -181,8 +188,8 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const uint16_t* __restr
   auto decode = [&](int64_t item) {
     Item w;
     w.bi = item / (ntr * ntc);
-    const int64_t rest = item % (ntr * ntc), tr = rest / ntc;
-    w.c0 = (rest % ntc) * 64;
+    const int64_t rest = item % (ntr * ntc), tr = rest % ntr;
+    w.c0 = (rest / ntr) * TC;
     if constexpr (SEG) {
       w.nrow = 0;
       w.nblk = 0;
@@ -204,13 +211,13 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const uint16_t* __restr
     }
     return w;
   };
-  v4u buf[8];
+  v4u buf[LD];
   auto load = [&](const Item& w) {
     const uint16_t* xb = x + in.base(w.bi);
-    const int cc = (tid & 7) * 8;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int rr = (tid >> 3) + 32 * i;
+    for (int i = 0; i < LD; ++i) {
+      const int q = tid + 256 * i;
+      const int rr = q / CPR, cc = (q % CPR) * 8;
       buf[i] = v4u{0, 0, 0, 0};
       if (rr < w.nrow && w.c0 + cc < cols)
         buf[i] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(xb + (w.r0 + rr) * in.sn + w.c0 + cc));
@@ -221,24 +228,24 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const uint16_t* __restr
   for (; item < nitems; item += gridDim.x) {
     const Item w = decode(item);
     if (vec8) {
-      const int cc = (tid & 7) * 8;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int rr = (tid >> 3) + 32 * i;
-        *reinterpret_cast<v4u*>(&tile[rr * 64 + (cc ^ (8 * i))]) = buf[i];
+      for (int i = 0; i < LD; ++i) {
+        const int q = tid + 256 * i;
+        const int rr = q / CPR, cc = (q % CPR) * 8;
+        *reinterpret_cast<v4u*>(&tile[rr * TC + (cc ^ (8 * (rr >> 5)))]) = buf[i];
       }
     } else {
       const uint16_t* xb = x + in.base(w.bi);
-      for (int i = tid; i < 256 * 64; i += 256) {
-        const int rr = i >> 6, cc = i & 63;
-        tile[rr * 64 + (cc ^ (8 * (rr >> 5)))] =
+      for (int i = tid; i < 256 * TC; i += 256) {
+        const int rr = i / TC, cc = i % TC;
+        tile[rr * TC + (cc ^ (8 * (rr >> 5)))] =
             (rr < w.nrow && w.c0 + cc < cols) ? xb[(w.r0 + rr) * in.sn + w.c0 + cc] : uint16_t(0);
       }
     }
     __syncthreads();
     if (vec8 && item + gridDim.x < nitems) load(decode(item + gridDim.x));
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < TC * 8 / 256; ++k) {
       const int it = tid + 256 * k;
       const int jb = it & 7, c = it >> 3;
       if (w.c0 + c >= cols || jb >= w.nblk) continue;
@@ -246,7 +253,7 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const uint16_t* __restr
       uint32_t m = 0;
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
-        const uint32_t h = tile[(32 * jb + i) * 64 + (c ^ (8 * jb))];
+        const uint32_t h = tile[(32 * jb + i) * TC + (c ^ (8 * jb))];
         m = max(m, h & 0x7FFFu);
         f[i] = __uint_as_float(h << 16);
       }
@@ -262,6 +269,24 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const uint16_t* __restr
     }
     __syncthreads();
   }
+}
+
+// Launch of the row-axis kernel: 128-column tiles unless the input is at
+// most 64 columns wide.
+template <int MODE, bool SEG>
+void launch_cols(const uint16_t* x, uint8_t* codes, uint8_t* scales, int64_t rows, int64_t cols, int64_t batch,
+                 int64_t ntr, int64_t vstride, const Layout3& in, const RowSegments& seg, int64_t grid_cap,
+                 hipStream_t stream) {
+  const int tc = cols > 64 ? 128 : 64;
+  const int64_t ntc = (cols + tc - 1) / tc;
+  const int64_t nitems = batch * ntr * ntc;
+  const int64_t grid = nitems < grid_cap ? nitems : grid_cap;
+  if (tc == 128)
+    quant_cols_kernel<MODE, SEG, 128><<<dim3(unsigned(grid)), dim3(256), 0, stream>>>(
+        x, codes, scales, rows, cols, ntr, ntc, nitems, vstride, in, seg);
+  else
+    quant_cols_kernel<MODE, SEG, 64><<<dim3(unsigned(grid)), dim3(256), 0, stream>>>(
+        x, codes, scales, rows, cols, ntr, ntc, nitems, vstride, in, seg);
 }
 
 // The varlen table from cu_seqlens (batch + 1 entries, device memory): four
@@ -347,9 +372,9 @@ __global__ __launch_bounds__(256) void varlen_table_kernel(const int* __restrict
 
 // Grid caps: the streaming kernel walks blocks with a grid stride (2^17
 // workgroups cover 2^30 elements in one pass; a cap of 2^16, two passes per
-// thread, ran 2^30 at 72% of HBM bandwidth against 75%); the column kernel's
-// workgroups each walk tiles (five 32 KiB tiles fit one CU's LDS, so 2560
-// workgroups are two rounds of 256 CUs x 5).
+// thread, ran 2^30 at 72% of HBM bandwidth against 75%); the row-axis
+// kernel's workgroups each walk tiles (two 64 KiB tiles fit one CU's LDS, so
+// 2560 workgroups are five rounds of 256 CUs x 2).
 constexpr int64_t kStreamGrid = 131072;
 constexpr int64_t kColsGrid = 2560;
 
@@ -381,17 +406,14 @@ hipError_t launch_quantize(const void* x, int64_t batch, int64_t rows, int64_t c
           static_cast<const uint16_t*>(x), reinterpret_cast<uint4*>(codes), scales, batch * rows, cols, nb);
   } else {
     const int64_t nb = (rows + 31) / 32;
-    const int64_t ntr = (rows + 255) / 256, ntc = (cols + 63) / 64;
-    const int64_t nitems = batch * ntr * ntc;
-    const int64_t grid = nitems < kColsGrid ? nitems : kColsGrid;
+    const int64_t ntr = (rows + 255) / 256;
     const Layout3 dense{1, rows * cols, 0, cols};
     const RowSegments none{nullptr, nullptr, nullptr, 0};
+    const uint16_t* xp = static_cast<const uint16_t*>(x);
     if (mode == kModeUOS)
-      quant_cols_kernel<kModeUOS, false><<<dim3(unsigned(grid)), dim3(256), 0, stream>>>(
-          static_cast<const uint16_t*>(x), codes, scales, rows, cols, ntr, ntc, nitems, nb, dense, none);
+      launch_cols<kModeUOS, false>(xp, codes, scales, rows, cols, batch, ntr, nb, dense, none, kColsGrid, stream);
     else
-      quant_cols_kernel<kModeOCP, false><<<dim3(unsigned(grid)), dim3(256), 0, stream>>>(
-          static_cast<const uint16_t*>(x), codes, scales, rows, cols, ntr, ntc, nitems, nb, dense, none);
+      launch_cols<kModeOCP, false>(xp, codes, scales, rows, cols, batch, ntr, nb, dense, none, kColsGrid, stream);
   }
   return hipGetLastError();
 }
@@ -421,16 +443,12 @@ hipError_t launch_quantize_strided(const void* x, int64_t B, int64_t H, int64_t 
                                                                              scales, rows, cols, in);
   } else {
     const int64_t nb = (rows + 31) / 32;
-    const int64_t ntr = (rows + 255) / 256, ntc = (cols + 63) / 64;
-    const int64_t nitems = B * H * ntr * ntc;
-    const int64_t grid = nitems < kColsGrid ? nitems : kColsGrid;
+    const int64_t ntr = (rows + 255) / 256;
     const RowSegments none{nullptr, nullptr, nullptr, 0};
     if (mode == kModeUOS)
-      quant_cols_kernel<kModeUOS, false><<<dim3(unsigned(grid)), dim3(256), 0, stream>>>(
-          xp, codes, scales, rows, cols, ntr, ntc, nitems, nb, in, none);
+      launch_cols<kModeUOS, false>(xp, codes, scales, rows, cols, B * H, ntr, nb, in, none, kColsGrid, stream);
     else
-      quant_cols_kernel<kModeOCP, false><<<dim3(unsigned(grid)), dim3(256), 0, stream>>>(
-          xp, codes, scales, rows, cols, ntr, ntc, nitems, nb, in, none);
+      launch_cols<kModeOCP, false>(xp, codes, scales, rows, cols, B * H, ntr, nb, in, none, kColsGrid, stream);
   }
   return hipGetLastError();
 }
@@ -453,16 +471,12 @@ hipError_t launch_quantize_varlen_cols(const void* x, int batch, int64_t T, int6
   const int n = batch + 1;
   const RowSegments seg{tab, tab + 2 * n, tab + 3 * n, batch};
   const Layout3 in{H, 0, sh, sn};
-  const int64_t ntr = (T + 255) / 256 + batch, ntc = (d + 63) / 64;
-  const int64_t nitems = H * ntr * ntc;
-  const int64_t grid = nitems < kColsGrid ? nitems : kColsGrid;
+  const int64_t ntr = (T + 255) / 256 + batch;
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   if (mode == kModeUOS)
-    quant_cols_kernel<kModeUOS, true><<<dim3(unsigned(grid)), dim3(256), 0, stream>>>(
-        xp, codes, scales, T, d, ntr, ntc, nitems, 0, in, seg);
+    launch_cols<kModeUOS, true>(xp, codes, scales, T, d, H, ntr, 0, in, seg, kColsGrid, stream);
   else
-    quant_cols_kernel<kModeOCP, true><<<dim3(unsigned(grid)), dim3(256), 0, stream>>>(
-        xp, codes, scales, T, d, ntr, ntc, nitems, 0, in, seg);
+    launch_cols<kModeOCP, true>(xp, codes, scales, T, d, H, ntr, 0, in, seg, kColsGrid, stream);
   return hipGetLastError();
 }
 
