@@ -73,7 +73,8 @@ def source_hash(src: str = "attention.hip") -> str:
     from mxfp4_quantized_attention_amd import build as hip_build
     h = hashlib.sha256()
     csrc = os.path.dirname(ATTN_SRC)
-    for path in (os.path.join(csrc, src), os.path.join(csrc, "mx_device.h")):
+    headers = () if src == "probe.hip" else ("mx_device.h",)  # the probe includes no header of ours
+    for path in (os.path.join(csrc, src), *(os.path.join(csrc, hdr) for hdr in headers)):
         with open(path, "rb") as f:
             h.update(f.read())
     fl = hip_build.flags()
