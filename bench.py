@@ -272,6 +272,27 @@ def quality_context(q, k, v, out_uos_pnq, out_ocp, nrows=64):
     return res
 
 
+def emit(result, checks):
+    """Print the JSON line with every in-run correctness check of the run.
+    If any failed, the line is marked invalid and the run exits with status 3,
+    so a number measured on wrong results is never taken for a valid one."""
+    result["checks"] = {name: bool(ok) for name, ok in checks.items()}
+    failed = [name for name, ok in checks.items() if not ok]
+    result["valid"] = not failed
+    print(json.dumps(result), flush=True)
+    if failed:
+        log(f"[bench] in-run check failed: {', '.join(failed)}; the line above is not a valid measurement")
+        sys.exit(3)
+
+
+def oracle_sample_ok(v):
+    """The attention baselines' agreement on their sample: every row not flagged
+    near a rounding tie within the base bound, and rel-L2 within 1e-3.  Flagged
+    rows may exceed the base bound by a flip budget the timed run does not
+    compute; the GPU tests check them against it."""
+    return v["max_diff_over_bound_unflagged_rows"] <= 1.0 and v["rel_l2"] <= 1e-3
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -438,7 +459,10 @@ def main():
         full = args.workload in ("tiny", "small")
         result["cpu_baseline"] = cpu_baseline(q, k, v, args.workload, mode, pnq, mx.kv_tile(d), gpu_out,
                                               **({"heads": B * H, "rows_per_head": N} if full else {}))
-    print(json.dumps(result), flush=True)
+    checks = {"step_equals_mxattn_fwd": same}
+    if "cpu_baseline" in result:
+        checks["oracle_agrees_on_sample"] = oracle_sample_ok(result["cpu_baseline"]["vs_gpu_on_sample"])
+    emit(result, checks)
 
 
 PROBE_OPS = {"fma": 1, "exp": 2, "cvt": 3, "max3": 4, "mfma": 5}
@@ -631,7 +655,10 @@ def gemm_bench(args, dev):
                       f"{dt:.1f} s; FLOP counted as 2*N*K per row",
             "max_diff_over_bound_on_sample": float((np.abs(got - ref["out"]) / (err + ulp)).max()),
         }
-    print(json.dumps(result), flush=True)
+    checks = {"step_equals_mxgemm": same}
+    if "cpu_baseline" in result:
+        checks["oracle_bound_on_sample"] = result["cpu_baseline"]["max_diff_over_bound_on_sample"] <= 1.0
+    emit(result, checks)
 
 
 def varlen_bench(args, dev):
@@ -745,7 +772,10 @@ def varlen_bench(args, dev):
             "max_diff_over_bound_unflagged_rows": float(over[~flagged].max()) if (~flagged).any() else 0.0,
             "flagged_rows": int(flagged.sum()),
         }
-    print(json.dumps(result), flush=True)
+    checks = {"step_equals_per_sequence_mxattn_fwd": same}
+    if "cpu_baseline" in result:
+        checks["oracle_agrees_on_sample"] = result["cpu_baseline"]["max_diff_over_bound_unflagged_rows"] <= 1.0
+    emit(result, checks)
 
 
 def block_bench(args, dev):
@@ -868,7 +898,7 @@ def block_bench(args, dev):
         "unfused_ms_per_step": ms_unfused,
         "fused_equals_unfused": same,
     }
-    print(json.dumps(result), flush=True)
+    emit(result, {"fused_equals_unfused": same})
 
 
 def quantize_sweep(args, dev):
@@ -928,6 +958,8 @@ def quantize_sweep(args, dev):
             head = row
             host_codes = codes.cpu().numpy()
             host_scales = scales.cpu().numpy()
+        if axis == 0:
+            rows_codes, rows_scales = codes.cpu().numpy(), scales.cpu().numpy()
     result = {
         "metric": "MXFP4 quantize GB/s (2.53125 B/element: bf16 in, E2M1 codes + E8M0 scales out) "
                   "and % of MI355X HBM peak",
@@ -969,7 +1001,23 @@ def quantize_sweep(args, dev):
             "per_size": per_size,
             "bit_exact_vs_gpu_on_sample": same,
         }
-    print(json.dumps(result), flush=True)
+        # the row-axis case (blocks along rows at 2^28) on 8192 seeded
+        # (column, block) pairs, every column represented
+        R, C = 1 << 18, 1024
+        x28 = workloads.sweep(28).reshape(R, C)
+        g = np.random.default_rng(2028)
+        nb = R // 32
+        cols = np.concatenate([np.arange(C), g.integers(0, C, 8192 - C)])
+        blks = np.concatenate([g.integers(0, nb, C - 2), [0, nb - 1], g.integers(0, nb, 8192 - C)])
+        sub = np.stack([x28[32 * b: 32 * b + 32, c] for c, b in zip(cols, blks)])
+        del x28
+        ec, es = oracle.quantize_bf16(sub, 1, sub.shape[0], 32, 1, oracle.MODE_UOS)
+        flat = cols.astype(np.int64) * nb + blks
+        same_rows = bool(np.array_equal(rows_codes.reshape(-1, 16)[flat].reshape(-1), ec.reshape(-1))
+                         and np.array_equal(rows_scales.reshape(-1)[flat], es.reshape(-1)))
+        result["cpu_baseline"]["rows_axis_2^28_bit_exact_on_sample"] = same_rows
+    emit(result, {"oracle_bit_exact_at_2^30": same, "oracle_bit_exact_rows_axis_2^28_sample": same_rows}
+         if "cpu_baseline" in result else {})
 
 
 if __name__ == "__main__":

@@ -1,7 +1,12 @@
 """bench.py's host-side pieces that need no GPU: the oracle baseline on a
 configuration small enough to time in full, and the argument clamping that
-keeps its sample inside the workload."""
+keeps its sample inside the workload, the vector-unit ceiling read from the
+committed probe summary, and the rule that a failed in-run check invalidates
+the line."""
+import json
+
 import numpy as np
+import pytest
 
 import bench
 import oracle
@@ -54,3 +59,23 @@ def test_valu_ceiling_from_the_committed_probe():
     # any plausible shader clock
     assert bench.valu_ceilings(128, probe, 2.4)["ceiling"] < 0.5 * bench.PEAK_FP4_TFLOPS
     assert abs(bench.valu_ceilings(64, probe, ghz)["ceiling"] * 2 - c["ceiling"]) < 1e-6 * c["ceiling"]
+
+
+def test_emit_marks_a_failed_check_and_exits(capsys):
+    """A bench line whose in-run check failed says so and ends the run with
+    status 3; one whose checks held is marked valid."""
+    bench.emit({"metric": "m", "value": 1.0}, {"a": True, "b": True})
+    line = json.loads(capsys.readouterr().out.strip())
+    assert line["valid"] is True and line["checks"] == {"a": True, "b": True}
+    with pytest.raises(SystemExit) as e:
+        bench.emit({"metric": "m", "value": 1.0}, {"a": True, "b": False})
+    assert e.value.code == 3
+    line = json.loads(capsys.readouterr().out.strip())
+    assert line["valid"] is False and line["checks"]["b"] is False
+
+
+def test_oracle_sample_agreement_rule():
+    ok = {"max_diff_over_bound_unflagged_rows": 0.9, "rel_l2": 2e-4}
+    assert bench.oracle_sample_ok(ok)
+    assert not bench.oracle_sample_ok(dict(ok, max_diff_over_bound_unflagged_rows=1.01))
+    assert not bench.oracle_sample_ok(dict(ok, rel_l2=2e-3))
