@@ -239,35 +239,51 @@ __global__ __launch_bounds__(kGWaves * 64) __attribute__((amdgpu_waves_per_eu(2)
   //
   // The plain GEMM runs a persistent grid (one workgroup per CU, see
   // persistent_grid): a workgroup walks the tiles lt, lt + slots, ... of its
-  // XCD's range, and the stores of one tile's Y drain while the next tile's
-  // first fills and steps run.  The QKV projection runs one tile per
-  // workgroup.
+  // XCD's range.  With an even number of K steps the last step computes from
+  // lds1, so the next tile's first fills go into lds0 before this tile's last
+  // MFMAs and its epilogue (which then stages Y through lds1 alone, in two
+  // halves): they land while Y is written.  The QKV projection runs one tile
+  // per workgroup.
   const int w = blockIdx.x;
   const int nslot = gridDim.x >> 3;  // workgroups per XCD (the grid is a multiple of 8)
-  int lt = w >> 3;
-  do {
-  const int lin = (w & 7) * a.per_xcd + lt;
-  if (lin >= a.ntiles) break;
-  const int tmc = a.ntiles / a.tn;
-  const int gsz = 8 * a.tn;
-  const int gid = lin / gsz, rr = lin % gsz;
-  const int gm = min(8, tmc - 8 * gid);
-  const int m0 = (8 * gid + rr % gm) * kGM, n0 = (rr / gm) * kGN;
-
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g4 = lane >> 4;
   const int wm = wave & 3, wn = wave >> 2;  // wave tile: rows 64 wm of X, rows 128 wn of W
   const int K = a.K, KC = K / 2, KS = K / 32;
   const int nsteps = (K + kGK - 1) / kGK;
+  const int tmc = a.ntiles / a.tn;
+  const int gsz = 8 * a.tn;
 
-  const uint8_t* xc_t = uniform_ptr(a.xc + int64_t(m0) * KC);
-  const uint8_t* wc_t = uniform_ptr(a.wc + int64_t(n0) * KC);
-  const uint8_t* xs_t = uniform_ptr(a.xs + int64_t(m0) * KS);
-  const uint8_t* ws_t = uniform_ptr(a.ws + int64_t(n0) * KS);
-  const int xc_bytes = __builtin_amdgcn_readfirstlane((a.M - m0) * KC);
-  const int wc_bytes = __builtin_amdgcn_readfirstlane((a.N - n0) * KC);
-  const int xs_bytes = __builtin_amdgcn_readfirstlane((a.M - m0) * KS);
-  const int ws_bytes = __builtin_amdgcn_readfirstlane((a.N - n0) * KS);
+  // operand sources of tile `lin`
+  struct Src {
+    const uint8_t *xc, *wc, *xs, *ws;
+    int xcb, wcb, xsb, wsb;
+    int m0, n0;
+  };
+  auto src_of = [&](int lin) {
+    const int gid = lin / gsz, rr = lin % gsz;
+    const int gm = min(8, tmc - 8 * gid);
+    Src t;
+    t.m0 = __builtin_amdgcn_readfirstlane((8 * gid + rr % gm) * kGM);
+    t.n0 = __builtin_amdgcn_readfirstlane((rr / gm) * kGN);
+    t.xc = uniform_ptr(a.xc + int64_t(t.m0) * KC);
+    t.wc = uniform_ptr(a.wc + int64_t(t.n0) * KC);
+    t.xs = uniform_ptr(a.xs + int64_t(t.m0) * KS);
+    t.ws = uniform_ptr(a.ws + int64_t(t.n0) * KS);
+    t.xcb = __builtin_amdgcn_readfirstlane((a.M - t.m0) * KC);
+    t.wcb = __builtin_amdgcn_readfirstlane((a.N - t.n0) * KC);
+    t.xsb = __builtin_amdgcn_readfirstlane((a.M - t.m0) * KS);
+    t.wsb = __builtin_amdgcn_readfirstlane((a.N - t.n0) * KS);
+    return t;
+  };
+  int lt = w >> 3;
+  bool prefetched = false;  // the previous tile already issued this tile's first fills into lds0
+  uint32_t sreg0 = 0, sreg1 = 0;
+  do {
+  const int lin = (w & 7) * a.per_xcd + lt;
+  if (lin >= a.ntiles) break;
+  const Src cur_src = src_of(lin);
+  const int m0 = cur_src.m0, n0 = cur_src.n0;
 
   // Code fills: 256 rows x 128 bytes per operand = 2048 16-byte pieces, four
   // per thread per operand.  Slot s = (wave + 8u) * 64 + lane of the region
@@ -286,23 +302,22 @@ __global__ __launch_bounds__(kGWaves * 64) __attribute__((amdgpu_waves_per_eu(2)
   const int srow = tid & 255;
   const uint32_t soff = uint32_t(srow * KS);
   const int sdst = ((srow & 15) * 16) + (srow >> 4);  // + (g * 16) * 16 per block g
-  uint32_t sreg0 = 0, sreg1 = 0;
 
-  auto issue = [&](int step, GemmLds& T) {
+  auto issue_from = [&](const Src& src, int step, GemmLds& T) {
     const int kb = step * kGK;
     const int sb = __builtin_amdgcn_readfirstlane(kb / 32);
     // waves 0-3 (threads 0-255) stage W scales, waves 4-7 X scales: the
     // choice is wave-uniform, so the descriptor stays scalar
     const __amdgpu_buffer_rsrc_t srs = wave < 4
-        ? __builtin_amdgcn_make_buffer_rsrc((void*)(ws_t + sb), 0, ws_bytes - sb, kBufferFlags)
-        : __builtin_amdgcn_make_buffer_rsrc((void*)(xs_t + sb), 0, xs_bytes - sb, kBufferFlags);
+        ? __builtin_amdgcn_make_buffer_rsrc((void*)(src.ws + sb), 0, src.wsb - sb, kBufferFlags)
+        : __builtin_amdgcn_make_buffer_rsrc((void*)(src.xs + sb), 0, src.xsb - sb, kBufferFlags);
     sreg0 = __builtin_amdgcn_raw_buffer_load_b32(srs, soff, 0, 0);
     sreg1 = __builtin_amdgcn_raw_buffer_load_b32(srs, soff + 4, 0, 0);
     const int cb = __builtin_amdgcn_readfirstlane(kb / 2);
     const __amdgpu_buffer_rsrc_t wrs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(wc_t + cb), 0, wc_bytes - cb, kBufferFlags);
+        __builtin_amdgcn_make_buffer_rsrc((void*)(src.wc + cb), 0, src.wcb - cb, kBufferFlags);
     const __amdgpu_buffer_rsrc_t xrs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(xc_t + cb), 0, xc_bytes - cb, kBufferFlags);
+        __builtin_amdgcn_make_buffer_rsrc((void*)(src.xc + cb), 0, src.xcb - cb, kBufferFlags);
     // (wave & 7): a provably small offset lets the compiler see that these
     // fills stay inside T and cannot alias reads of the other buffer
 #pragma unroll
@@ -312,6 +327,7 @@ __global__ __launch_bounds__(kGWaves * 64) __attribute__((amdgpu_waves_per_eu(2)
     for (int u = 0; u < 4; ++u)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (lds_ptr)(T.x + ((wave & 7) + kGWaves * u) * 1024), 16, foff[u], 0, 0, 0);
   };
+  auto issue = [&](int step, GemmLds& T) { issue_from(cur_src, step, T); };
   auto finish = [&](GemmLds& T) {
     uint8_t* sl = wave < 4 ? &T.wsl[0][0] : &T.xsl[0][0];
 #pragma unroll
@@ -385,7 +401,7 @@ __global__ __launch_bounds__(kGWaves * 64) __attribute__((amdgpu_waves_per_eu(2)
     finish(nxt);
     __syncthreads();
   };
-  issue(0, lds0);
+  if (!prefetched) issue(0, lds0);
   finish(lds0);
   __syncthreads();
   int s = 0;
@@ -398,6 +414,13 @@ __global__ __launch_bounds__(kGWaves * 64) __attribute__((amdgpu_waves_per_eu(2)
     step(s, lds0, lds1);
     last = &lds1;
   }
+  // The next tile's first fills go out now, into lds0, when the last step
+  // computes from lds1 (an even number of steps): lds0 is free, and the
+  // fills land while this tile finishes and writes Y.
+  const int lt_next = lt + nslot;
+  const int lin_next = (w & 7) * a.per_xcd + lt_next;
+  const bool pf = EPI == 0 && (nsteps & 1) == 0 && lt_next < a.per_xcd && lin_next < a.ntiles;
+  if (pf) issue_from(src_of(lin_next), 0, lds0);
   if (half_last)
     compute(*last, one_chunk);
   else
@@ -409,41 +432,52 @@ __global__ __launch_bounds__(kGWaves * 64) __attribute__((amdgpu_waves_per_eu(2)
     qkv_epilogue<MODE>(a, acc, lds0, lds1, m0, n0, wm, wn, wave, lane);
     break;
   }
-  // Y through LDS: the bf16 tile is staged in the operand buffers, then each
-  // wave writes 32 whole rows of it, two per instruction (32 lanes x 16 bytes
-  // = one 512-byte row), with nontemporal stores.  Against 8-byte stores
-  // straight from the accumulators (16 rows x 32 bytes per instruction) this
-  // took the DiT FFN shape from 1.46-1.54 ms to 1.25-1.27 ms.
-  uint8_t* t0 = reinterpret_cast<uint8_t*>(&lds0);
-  uint8_t* t1 = reinterpret_cast<uint8_t*>(&lds1);
+  // Y through LDS, in two halves through the last step's buffer (the other
+  // one may hold the next tile's first fills): half h holds rows
+  // 64 wm + 32 h + [0, 32) of every wave row, i.e. accumulators i = 2h, 2h+1,
+  // as staged row 32 wm + 16 (i & 1) + r16.  Each wave then writes 16 whole
+  // rows of the half, two per instruction (32 lanes x 16 bytes = one 512-byte
+  // row), with nontemporal stores.
+  uint8_t* tl = reinterpret_cast<uint8_t*>(const_cast<GemmLds*>(last));
   __syncthreads();  // every wave has finished reading the operand tiles
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 64 * wm + 16 * i + r16;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int n = 128 * wn + 16 * j + 4 * g4;
-      const uint32_t b0 = f32_to_bf16_rne(acc[j][i][0]), b1 = f32_to_bf16_rne(acc[j][i][1]);
-      const uint32_t b2 = f32_to_bf16_rne(acc[j][i][2]), b3 = f32_to_bf16_rne(acc[j][i][3]);
-      *reinterpret_cast<uint2*>(tile_elem(t0, t1, r, n)) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
-    }
-  }
-  __syncthreads();
   const int cc = lane & 31, n = n0 + 8 * cc;
   const bool vec = (a.N & 7) == 0;  // 16-byte aligned rows
-#pragma unroll 4
-  for (int k = 0; k < 16; ++k) {
-    const int r = 32 * wave + 2 * k + (lane >> 5), m = m0 + r;
-    if (m >= a.M || n >= a.N) continue;
-    const v4u v = *reinterpret_cast<const v4u*>(tile_elem(t0, t1, r, 8 * cc));
-    uint16_t* dst = a.y + int64_t(m) * a.N + n;
-    if (vec) {
-      __builtin_nontemporal_store(v, reinterpret_cast<v4u*>(dst));
-    } else {
-      for (int e = 0; e < 8 && n + e < a.N; ++e) dst[e] = uint16_t(v[e >> 1] >> (16 * (e & 1)));
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (h) __syncthreads();  // the first half's rows have been read
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+      const int i = 2 * h + ii;
+      const int sr = 32 * wm + 16 * ii + r16;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int nn = 128 * wn + 16 * j + 4 * g4;
+        const uint32_t b0 = f32_to_bf16_rne(acc[j][i][0]), b1 = f32_to_bf16_rne(acc[j][i][1]);
+        const uint32_t b2 = f32_to_bf16_rne(acc[j][i][2]), b3 = f32_to_bf16_rne(acc[j][i][3]);
+        *reinterpret_cast<uint2*>(tl + sr * 512 + (((nn >> 3) ^ (sr & 31)) << 4) + (nn & 7) * 2) =
+            make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+      }
+    }
+    __syncthreads();
+#pragma unroll 2
+    for (int k = 0; k < 8; ++k) {
+      const int sr = 16 * wave + 2 * k + (lane >> 5);
+      const int m = m0 + 64 * (sr >> 5) + 32 * h + (sr & 31);
+      if (m >= a.M || n >= a.N) continue;
+      const v4u v = *reinterpret_cast<const v4u*>(tl + sr * 512 + ((cc ^ (sr & 31)) << 4));
+      uint16_t* dst = a.y + int64_t(m) * a.N + n;
+      if (vec) {
+        __builtin_nontemporal_store(v, reinterpret_cast<v4u*>(dst));
+      } else {
+        for (int e = 0; e < 8 && n + e < a.N; ++e) dst[e] = uint16_t(v[e >> 1] >> (16 * (e & 1)));
+      }
     }
   }
-  __syncthreads();  // the next tile's fills reuse the staging buffers; the stores drain meanwhile
+  // the next tile's barrier (after its first fills land) orders these reads
+  // before the fills that reuse this buffer; without a prefetch its first
+  // fills go to lds0 right away, so wait here
+  if (!pf) __syncthreads();
+  prefetched = pf;
   lt += nslot;
   } while (EPI == 0 && lt < a.per_xcd);
 }
@@ -452,8 +486,9 @@ namespace {
 
 // The plain GEMM's grid: one workgroup per CU (its LDS holds one), rounded
 // down to a multiple of 8 so every XCD gets the same number of slots, and no
-// more workgroups than tiles.  (Persistent: 1.22-1.25 ms against 1.26 ms for
-// one workgroup per tile on the DiT FFN shape, identical results.)
+// more workgroups than tiles.  (On the DiT FFN shape, identical results:
+// one workgroup per tile 1.34 ms, persistent 1.27 ms, persistent with the
+// next tile's first fills issued before the epilogue 1.21-1.24 ms.)
 int persistent_grid(const GemmArgs& a) {
   static int cus = 0;
   if (cus == 0) {
