@@ -75,6 +75,22 @@ def test_gemm_dit_shape_sampled_rows(omode, gmode):
     compare_gemm(to_np_u16(y)[rows], ref, K, what=f"gemm dit {gmode} (64 rows)")
 
 
+@pytest.mark.parametrize("K", [384, 512, 640])
+def test_gemm_several_tiles_per_workgroup(K):
+    """17 x 17 tiles of 256 x 256 over a grid of one workgroup per CU, so some
+    workgroups take a second tile: with an even number of 256-deep K steps
+    (K = 384 with a half last step, K = 512) the second tile's first fills are
+    issued before the first tile's epilogue; K = 640 (odd) takes the plain
+    path.  256 seeded rows, the last M tile included."""
+    M, N = 4113, 4196
+    x, w = workloads.gemm_inputs(M=M, N=N, K=K, seed=K)
+    y, _ = run_gemm(x, w, M, N, K, "uos")
+    rows = np.sort(np.concatenate([np.random.default_rng(K).choice(M - 17, 240, replace=False),
+                                   np.arange(M - 16, M)]))
+    ref = oracle.gemm_rows(x, w, M, N, K, oracle.MODE_UOS, rows)
+    compare_gemm(to_np_u16(y)[rows], ref, K, what=f"gemm {M}x{N}x{K} (256 rows)")
+
+
 @pytest.mark.parametrize("gmode", ["uos", "ocp"])
 def test_gemm_bf16_entry_equals_quantized_entry(gmode):
     M, N, K = 777, 512, 1280
