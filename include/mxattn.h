@@ -39,8 +39,10 @@
  *     GEMM outputs are accumulated in fp32, so they must also fit fp32: a
  *     product of the dequantized operands that overflows fp32 is outside the
  *     supported range.
- *   - The library keeps no global state; calls on different streams may run
- *     concurrently as long as they do not write the same buffers.
+ *   - The library keeps no global state apart from mxattn_fwd_noalloc's
+ *     device array (see there); every other call may run concurrently with
+ *     others on different streams as long as they do not write the same
+ *     buffers.
  */
 #ifndef MXATTN_H
 #define MXATTN_H

@@ -490,13 +490,11 @@ namespace {
 // one workgroup per tile 1.34 ms, persistent 1.27 ms, persistent with the
 // next tile's first fills issued before the epilogue 1.21-1.24 ms.)
 int persistent_grid(const GemmArgs& a) {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0;
-    hipDeviceProp_t prop;
-    if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess)
-      cus = prop.multiProcessorCount;
-    if (cus < 8) cus = 8;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8) {
+    (void)hipGetLastError();
+    return a.per_xcd * 8;  // one workgroup per tile
   }
   const int g = (cus / 8) * 8;
   return g < a.per_xcd * 8 ? g : a.per_xcd * 8;
