@@ -297,7 +297,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=10,
+                    help="untimed steps first: the clocks of a fresh process take about 20 ms of steady MFMA load to settle")
     ap.add_argument("--workload", default="wan", choices=["tiny", "small", "wan", "hunyuan", "sweep", "gemm", "wan_varlen",
                                                           "wan_block", "valu_probe"])
     ap.add_argument("--probe-out", default="", help="valu_probe: also write the summary JSON here")
