@@ -466,7 +466,9 @@ def main():
     emit(result, checks)
 
 
-PROBE_OPS = {"fma": 1, "exp": 2, "cvt": 3, "max3": 4, "mfma": 5}
+PROBE_OPS = {"fma": 1, "exp": 2, "cvt": 3, "max3": 4, "mfma": 5, "mfma32": 6, "mfma_f8": 7}
+# FLOP of one wave instruction of each scaled MFMA form the probe times
+PROBE_MFMA_FLOP = {"mfma": 2 * 16 * 16 * 128, "mfma32": 2 * 32 * 32 * 64, "mfma_f8": 2 * 16 * 16 * 128}
 
 
 def probe_bench(args, dev):
@@ -524,6 +526,16 @@ def probe_bench(args, dev):
         tab = run(PROBE_OPS[name], iters[name], PROBE_OPS["mfma"], iters["mfma"])
         overlap[name] = (ta + tb - tab) / min(ta, tb)
         log(f"[probe] {name} + mfma: alone {ta:.3f} / {tb:.3f} ms, together {tab:.3f} ms, overlap {overlap[name]:.2f}")
+    log("[probe] overlap with the other MFMA forms on other waves of the same SIMD")
+    overlap_forms = {}
+    for form in ("mfma32", "mfma_f8"):
+        overlap_forms[form] = {}
+        tb = run(0, 0, PROBE_OPS[form], iters[form])
+        for name in ("fma", "exp", "cvt", "max3"):
+            ta = run(PROBE_OPS[name], iters[name])
+            tab = run(PROBE_OPS[name], iters[name], PROBE_OPS[form], iters[form])
+            overlap_forms[form][name] = (ta + tb - tab) / min(ta, tb)
+            log(f"[probe] {name} + {form}: overlap {overlap_forms[form][name]:.2f}")
     log("[probe] one MFMA and R vector instructions interleaved in one wave")
     mixed = {}
     for name in ("fma", "exp", "cvt", "max3"):
@@ -546,6 +558,9 @@ def probe_bench(args, dev):
         "slots": {k: v / slot for k, v in cost.items()},
         "slots_per_score": slots,
         "overlap_with_mfma_other_waves": overlap,
+        "mfma_forms": {k: {"ns": cost[k], "pflops_1024_simds": PROBE_MFMA_FLOP[k] * 1024 / cost[k] / 1e6}
+                       for k in PROBE_MFMA_FLOP},
+        "overlap_with_other_mfma_forms": overlap_forms,
         "mfma_interleaved_same_wave": mixed,
     }
     print(json.dumps(summary), flush=True)

@@ -16,7 +16,10 @@
 // issue throughput is measured).  The kernel time with both roles busy,
 // against each role alone, gives the overlap of the two instruction streams
 // on one SIMD.  The interleaved ops put one scaled FP4 MFMA and R vector
-// instructions of one kind into the same wave's stream.
+// instructions of one kind into the same wave's stream.  Two other scaled
+// MFMA forms are timed as well, for the choice of shape: the 32x32x64 FP4
+// form (the same FLOP rate in half the instructions) and the 16x16x128 FP8
+// form.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -29,12 +32,15 @@ enum : int {
   kCvt = 3,
   kMax3 = 4,
   kMfma = 5,
+  kMfma32 = 6,  // v_mfma_scale_f32_32x32x64_f8f6f4, FP4 operands
+  kMfmaF8 = 7,  // v_mfma_scale_f32_16x16x128_f8f6f4, FP8 (E4M3) operands
   // one MFMA then R instructions of a vector op, 8 times per iteration
   kMixBase = 16,  // kMixBase + 4 * R + vector op (kFma, kExp, kCvt, kMax3), R in {1, 2, 4, 8}
 };
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ void fma8(float (&a)[8], float b, float c) {
   asm volatile(
@@ -96,6 +102,19 @@ struct State {
 // R instructions of vector op VOP, 8 times per iteration.
 template <int OP, int VOP = 0, int R = 0>
 __device__ __forceinline__ void loop(State& st, int iters) {
+  if constexpr (OP == kMfma32) {
+    // one accumulator chain, local to this path, so its 16 registers are not
+    // held by the kernel's other paths (the probe runs 8 waves per SIMD, at
+    // most 64 VGPRs)
+    v16f acc32 = {};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+        acc32 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(st.A, st.B, acc32, 4, 4, 0, st.sa, 0, st.sb);
+    }
+    st.a[0] += acc32[0] + acc32[15];
+    return;
+  }
   for (int it = 0; it < iters; ++it) {
     if constexpr (OP == kFma) fma8(st.a, st.b, st.c);
     else if constexpr (OP == kExp) exp8(st.a);
@@ -104,6 +123,11 @@ __device__ __forceinline__ void loop(State& st, int iters) {
     else if constexpr (OP == kMfma) {
 #pragma unroll
       for (int m = 0; m < 8; ++m) st.acc[m & 3] = mfma(st.A, st.B, st.acc[m & 3], st.sa, st.sb);
+    } else if constexpr (OP == kMfmaF8) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+        st.acc[m & 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(st.A, st.B, st.acc[m & 3], 0, 0, 0, st.sa, 0,
+                                                                          st.sb);
     } else {
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
@@ -133,8 +157,8 @@ __device__ __forceinline__ void run_op(int op, int iters, float* out, int gid) {
   st.b = 0.999f;
   st.c = 1e-4f * float(lane);
   st.sc = 1.0f;
-  st.A = v8i{0x22222222 + lane, 0x13131313, 0x24242424, 0x31313131, 0, 0, 0, 0};
-  st.B = v8i{0x21212121, 0x12121212 + lane, 0x23232323, 0x32323232, 0, 0, 0, 0};
+  st.A = v8i{0x22222222 + lane, 0x13131313, 0x24242424, 0x31313131, 0x22222222, 0x13131313, 0x24242424, 0x31313131};
+  st.B = v8i{0x21212121, 0x12121212 + lane, 0x23232323, 0x32323232, 0x21212121, 0x12121212, 0x23232323, 0x32323232};
 #pragma unroll
   for (int i = 0; i < 4; ++i) st.acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
   st.sa = 127;
@@ -146,6 +170,8 @@ __device__ __forceinline__ void run_op(int op, int iters, float* out, int gid) {
     case kCvt: loop<kCvt>(st, iters); break;
     case kMax3: loop<kMax3>(st, iters); break;
     case kMfma: loop<kMfma>(st, iters); break;
+    case kMfma32: loop<kMfma32>(st, iters); break;
+    case kMfmaF8: loop<kMfmaF8>(st, iters); break;
     default: {
       const int vop = op - kMixBase;  // kMixBase + 4 * R + (VOP & 3)
       const int r = vop >> 2;
@@ -162,6 +188,7 @@ __device__ __forceinline__ void run_op(int op, int iters, float* out, int gid) {
   for (int i = 0; i < 8; ++i) s += st.a[i];
 #pragma unroll
   for (int i = 0; i < 4; ++i) s += st.acc[i][0] + st.acc[i][1] + st.acc[i][2] + st.acc[i][3];
+
   // the results only keep the work alive; one store per wave
   if (lane == 0) out[gid] = s;
 }
@@ -195,7 +222,9 @@ extern "C" {
 // error code.
 int mxprobe_launch(int op_a, int iters_a, int op_b, int iters_b, int wg_per_cu, float* out,
                    unsigned long long* clocks, void* stream) {
-  if (wg_per_cu < 1 || wg_per_cu > 8 || iters_a < 0 || iters_b < 0 || !out || !clocks) return -1;
+  auto valid = [](int op) { return (op >= kNone && op <= kMfmaF8) || (op >= kMixBase + 4 && op < kMixBase + 36); };
+  if (wg_per_cu < 1 || wg_per_cu > 8 || iters_a < 0 || iters_b < 0 || !out || !clocks || !valid(op_a) || !valid(op_b))
+    return -1;
   probe_kernel<<<dim3(256 * wg_per_cu), dim3(512), 0, static_cast<hipStream_t>(stream)>>>(op_a, iters_a, op_b,
                                                                                           iters_b, out, clocks);
   return int(hipGetLastError());
