@@ -79,3 +79,15 @@ def test_oracle_sample_agreement_rule():
     assert bench.oracle_sample_ok(ok)
     assert not bench.oracle_sample_ok(dict(ok, max_diff_over_bound_unflagged_rows=1.01))
     assert not bench.oracle_sample_ok(dict(ok, rel_l2=2e-3))
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """Only one GPU is measured: --gpus 2 exits with status 2 and says so,
+    before anything touches a GPU."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], cwd=root, capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
